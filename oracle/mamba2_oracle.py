@@ -1,0 +1,183 @@
+"""CPU oracle for the Mamba2 temporal scan, forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  The HIP library never
+calls it and shares no code with it.
+
+Everything is plain numpy in float64: inputs are widened from float32, every
+step is the textbook definition, written in the order the pages give it.  A
+library matrix product serves as the projection step; nothing is blocked,
+fused or reordered beyond that.
+
+Sources (foxhunt pages):
+  * "Custom Kernel Optimization Implementation Plan", Task 1 (Mamba2 forward:
+    cuBLAS projections + lightweight scan) and Task 2 (Mamba2 backward: reverse
+    scan + weight-gradient GEMMs).
+  * "Custom Kernel Optimization -- cuBLAS Projections + Batch-Parallel Scans",
+    Design section 1 (Mamba2 scan: forward steps 1-2, backward steps 1-3).
+
+Notation: H = h_history[B, K, SH2] (row b*K+t of the flattened [B*K, SH2]
+matrix is sample b at history step t; t = K-1 is the newest), h_s2[B, SH2],
+W_A, W_B, W_C[SH2, D] (element (j, s) is row j, column s), D = STATE_D.
+
+Readings taken where the pages are silent or disagree (each also listed in the
+design notes):
+  * context is per state: context[b, s] = c[b, s] * x_K[b, s] (design spec,
+    forward step 2); the plan's sum over s into h_enriched is a later step.
+  * W_C projects h_s2 in the forward (both pages), so upstream d_context[B, D]
+    is given and dW_C = h_s2^T d_c with d_c = d_context * x_K.
+  * The reverse scan starts from dx_K = d_context * c (chain rule; the plan's
+    comment states it, its code line drops the factor c).
+  * x_0 = 0, no biases, no stability multiplier (the isv signal is absent).
+  * Weight gradients overwrite; they are not accumulated into.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def project(rows, W) -> np.ndarray:
+    """Projection rows @ W in float64.
+
+    Plan, Task 1 step 2 / design spec forward step 1: A_vals = h_history @ W_A,
+    B_vals = h_history @ W_B over the flattened [B*K, SH2] history, and
+    C_vals = h_s2 @ W_C.
+    """
+    return _f64(rows) @ _f64(W)
+
+
+def logistic(a) -> np.ndarray:
+    """Gate sigma(a) = 1 / (1 + exp(-a)) (plan Task 1 step 3; design spec step 2).
+
+    For a < 0 the equal form exp(a) / (1 + exp(a)) is used so that no
+    intermediate overflows; the value is the same function.
+    """
+    a = _f64(a)
+    out = np.empty_like(a)
+    pos = a >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-a[pos]))
+    e = np.exp(a[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def scan_forward(a, bb):
+    """Gated recurrence over the K history steps for every (sample, state).
+
+    x_0 = 0 and x_{t+1} = sigma(a_t) * x_t + b_t for t = 0 .. K-1 in storage
+    order (plan Task 1 step 3; design spec forward step 2).
+
+    Returns (g[B, K, D], x[B, K+1, D]) with x[:, t] the state *before* step t
+    is applied and x[:, K] the final state.
+    """
+    a = _f64(a)
+    bb = _f64(bb)
+    B, K, D = a.shape
+    g = logistic(a)
+    x = np.zeros((B, K + 1, D))
+    for t in range(K):
+        x[:, t + 1] = g[:, t] * x[:, t] + bb[:, t]
+    return g, x
+
+
+@dataclass
+class Forward:
+    a: np.ndarray        # [B, K, D] gate logits  H @ W_A
+    bb: np.ndarray       # [B, K, D] inputs       H @ W_B
+    c: np.ndarray        # [B, D]    readout      h_s2 @ W_C
+    g: np.ndarray        # [B, K, D] gates
+    x: np.ndarray        # [B, K+1, D] states, x[:, 0] = 0
+    context: np.ndarray  # [B, D]    c * x_K
+
+
+def forward(h_history, h_s2, W_A, W_B, W_C) -> Forward:
+    """Forward pass: three projections, the scan, then context = c * x_K."""
+    H = _f64(h_history)
+    B, K, SH2 = H.shape
+    rows = H.reshape(B * K, SH2)
+    a = project(rows, W_A).reshape(B, K, -1)
+    bb = project(rows, W_B).reshape(B, K, -1)
+    c = project(h_s2, W_C)
+    g, x = scan_forward(a, bb)
+    context = c * x[:, K]
+    return Forward(a=a, bb=bb, c=c, g=g, x=x, context=context)
+
+
+def context_from_projections(a, bb, c) -> np.ndarray:
+    """context = c * x_K from given projections (used to differentiate numerically)."""
+    _, x = scan_forward(a, bb)
+    return _f64(c) * x[:, -1]
+
+
+def scan_backward(g, x, c, d_context):
+    """Reverse scan (plan Task 2 step 2; design spec backward step 2).
+
+    L = sum_{b,s} d_context[b, s] * context[b, s] defines every gradient.
+      dx_K = d_context * c          d_c = d_context * x_K
+      for t = K-1 down to 0:
+        d_b[t] = dx_t
+        d_a[t] = dx_t * x_t * sigma'(a_t),  sigma' = g * (1 - g)
+        dx_{t}  <- dx_t * g_t   (gradient w.r.t. the state before step t)
+    The last dx (w.r.t. x_0 = 0, a constant) is discarded.
+    """
+    g = _f64(g)
+    x = _f64(x)
+    d_context = _f64(d_context)
+    B, K, D = g.shape
+    dx = d_context * _f64(c)
+    d_c = d_context * x[:, K]
+    d_a = np.empty((B, K, D))
+    d_b = np.empty((B, K, D))
+    for t in range(K - 1, -1, -1):
+        gt = g[:, t]
+        d_b[:, t] = dx
+        d_a[:, t] = dx * x[:, t] * gt * (1.0 - gt)
+        dx = dx * gt
+    return d_a, d_b, d_c
+
+
+@dataclass
+class Backward:
+    d_a: np.ndarray   # [B, K, D]
+    d_b: np.ndarray   # [B, K, D]
+    d_c: np.ndarray   # [B, D]
+    dW_A: np.ndarray  # [SH2, D]
+    dW_B: np.ndarray  # [SH2, D]
+    dW_C: np.ndarray  # [SH2, D]
+
+
+def backward(fwd: Forward, h_history, h_s2, d_context) -> Backward:
+    """Backward pass: reverse scan, then the three weight-gradient products.
+
+    dW_A = H^T d_a and dW_B = H^T d_b over the B*K history rows, and
+    dW_C = h_s2^T d_c over the B samples (plan Task 2 step 3; design spec
+    backward step 3).
+    """
+    H = _f64(h_history)
+    B, K, SH2 = H.shape
+    d_a, d_b, d_c = scan_backward(fwd.g, fwd.x, fwd.c, d_context)
+    rows = H.reshape(B * K, SH2)
+    D = d_c.shape[1]
+    dW_A = rows.T @ d_a.reshape(B * K, D)
+    dW_B = rows.T @ d_b.reshape(B * K, D)
+    dW_C = _f64(h_s2).T @ d_c
+    return Backward(d_a=d_a, d_b=d_b, d_c=d_c, dW_A=dW_A, dW_B=dW_B, dW_C=dW_C)
+
+
+def fwd_bwd(inputs: dict):
+    """One forward + backward step on a dict from the seeded input generator."""
+    f = forward(inputs["h_history"], inputs["h_s2"], inputs["W_A"], inputs["W_B"], inputs["W_C"])
+    b = backward(f, inputs["h_history"], inputs["h_s2"], inputs["d_context"])
+    return f, b
+
+
+def loss(h_history, h_s2, W_A, W_B, W_C, d_context) -> float:
+    """The scalar L = sum(d_context * context) whose gradients backward() returns."""
+    f = forward(h_history, h_s2, W_A, W_B, W_C)
+    return float(np.sum(_f64(d_context) * f.context))
