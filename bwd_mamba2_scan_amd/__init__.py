@@ -1,0 +1,238 @@
+"""Python binding of libmamba2scan.so, the MI355X Mamba2 temporal scan.
+
+Argument marshalling only: every step of the forward and backward runs in the
+library's HIP kernels.  PyTorch supplies device memory and the stream.  There
+is no CPU or PyTorch fallback: if the library is not built, every call raises.
+
+The entry points mirror include/mamba2_scan.h:
+    fwd(h_history, h_s2, W_A, W_B, W_C)         -> (context, saved)
+    bwd(h_history, h_s2, saved, d_context)      -> dict(dW_A, dW_B, dW_C[, d_a, d_b, d_c])
+    bwd_partials(...), bwd_reduce(...)          -- the two phases of bwd
+    saved_bytes(B, K, SH2, D), workspace_bytes(B, K, SH2, D)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmamba2scan.so")
+HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "mamba2_scan.h")
+
+OK = 0
+EBADDIM = -1
+EUNSUPPORTED = -2
+ENULL = -3
+ESIZE = -4
+EALIGN = -5
+EHIP = -6
+
+
+class Mamba2ScanError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+_lib = None
+
+_c_int = ctypes.c_int
+_c_size = ctypes.c_size_t
+_c_vp = ctypes.c_void_p
+
+_SIGNATURES = {
+    "mamba2_scan_saved_bytes": (_c_size, [_c_int] * 4),
+    "mamba2_scan_bwd_workspace_bytes": (_c_size, [_c_int] * 4),
+    "mamba2_scan_fwd": (_c_int, [_c_int] * 4 + [_c_vp] * 7 + [_c_size, _c_vp]),
+    "mamba2_scan_bwd": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 8 + [_c_size, _c_vp]),
+    "mamba2_scan_bwd_partials": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 5 + [_c_size, _c_vp]),
+    "mamba2_scan_bwd_reduce": (_c_int, [_c_int] * 4 + [_c_vp, _c_size] + [_c_vp] * 4),
+    "mamba2_scan_strerror": (ctypes.c_char_p, [_c_int]),
+}
+
+
+def lib():
+    """The loaded ctypes handle; raises if the library has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m bwd_mamba2_scan_amd.build` "
+                "(there is no fallback implementation)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/mamba2_scan.h declares."""
+    with open(HEADER) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba2_scan_\w+)\s*\(", text)))
+
+
+def strerror(status: int) -> str:
+    return lib().mamba2_scan_strerror(status).decode()
+
+
+def saved_bytes(B: int, K: int, SH2: int, D: int) -> int:
+    return int(lib().mamba2_scan_saved_bytes(B, K, SH2, D))
+
+
+def workspace_bytes(B: int, K: int, SH2: int, D: int) -> int:
+    return int(lib().mamba2_scan_bwd_workspace_bytes(B, K, SH2, D))
+
+
+# ----------------------------------------------------------------- torch side
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32 (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dims(h_history, D):
+    B, K, SH2 = (int(v) for v in h_history.shape)
+    return B, K, SH2, int(D)
+
+
+def _raise(status, where):
+    if status != OK:
+        raise Mamba2ScanError(status, where)
+
+
+def alloc_saved(B, K, SH2, D, device):
+    torch = _torch()
+    n = saved_bytes(B, K, SH2, D)
+    if n == 0:
+        raise ValueError(f"unsupported dimensions B={B} K={K} SH2={SH2} D={D}")
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def alloc_workspace(B, K, SH2, D, device):
+    torch = _torch()
+    n = workspace_bytes(B, K, SH2, D)
+    if n == 0:
+        raise ValueError(f"unsupported dimensions B={B} K={K} SH2={SH2} D={D}")
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def fwd(h_history, h_s2, W_A, W_B, W_C, *, context=None, saved=None, stream=None):
+    """Forward scan.  Returns (context [B, D], saved) -- saved feeds bwd()."""
+    torch = _torch()
+    if h_history.dim() != 3 or W_A.dim() != 2:
+        raise ValueError("h_history must be [B, K, SH2] and W_A [SH2, D]")
+    B, K, SH2, D = _dims(h_history, W_A.shape[1])
+    dev = h_history.device
+    _check(h_history, "h_history", (B, K, SH2), None)
+    _check(h_s2, "h_s2", (B, SH2), dev)
+    for name, w in (("W_A", W_A), ("W_B", W_B), ("W_C", W_C)):
+        _check(w, name, (SH2, D), dev)
+    if context is None:
+        context = torch.empty((B, D), dtype=torch.float32, device=dev)
+    _check(context, "context", (B, D), dev)
+    if saved is None:
+        saved = alloc_saved(B, K, SH2, D, dev)
+    _check(saved, "saved", None, dev)
+    st = lib().mamba2_scan_fwd(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(W_A), _ptr(W_B), _ptr(W_C),
+                               _ptr(context), _ptr(saved), saved.numel() * 4, _stream(stream, dev))
+    _raise(st, "mamba2_scan_fwd")
+    return context, saved
+
+
+def _bwd_args(h_history, h_s2, saved, d_context):
+    if h_history.dim() != 3 or d_context.dim() != 2:
+        raise ValueError("h_history must be [B, K, SH2] and d_context [B, D]")
+    B, K, SH2, D = _dims(h_history, d_context.shape[1])
+    dev = h_history.device
+    _check(h_history, "h_history", (B, K, SH2), None)
+    _check(h_s2, "h_s2", (B, SH2), dev)
+    _check(saved, "saved", None, dev)
+    _check(d_context, "d_context", (B, D), dev)
+    return B, K, SH2, D, dev
+
+
+def _debug_bufs(debug, B, K, D, dev):
+    torch = _torch()
+    if not debug:
+        return None, None, None
+    return (torch.empty((B, K, D), dtype=torch.float32, device=dev),
+            torch.empty((B, K, D), dtype=torch.float32, device=dev),
+            torch.empty((B, D), dtype=torch.float32, device=dev))
+
+
+def bwd(h_history, h_s2, saved, d_context, *, workspace=None, out=None, debug=False, stream=None):
+    """Backward scan.  Returns dict with dW_A, dW_B, dW_C [SH2, D] (and d_a, d_b, d_c if debug)."""
+    torch = _torch()
+    B, K, SH2, D, dev = _bwd_args(h_history, h_s2, saved, d_context)
+    if workspace is None:
+        workspace = alloc_workspace(B, K, SH2, D, dev)
+    _check(workspace, "workspace", None, dev)
+    if out is None:
+        out = {n: torch.empty((SH2, D), dtype=torch.float32, device=dev) for n in ("dW_A", "dW_B", "dW_C")}
+    for n in ("dW_A", "dW_B", "dW_C"):
+        _check(out[n], n, (SH2, D), dev)
+    d_a, d_b, d_c = _debug_bufs(debug, B, K, D, dev)
+    st = lib().mamba2_scan_bwd(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(saved), saved.numel() * 4,
+                               _ptr(d_context), _ptr(out["dW_A"]), _ptr(out["dW_B"]), _ptr(out["dW_C"]),
+                               _ptr(d_a), _ptr(d_b), _ptr(d_c), _ptr(workspace), workspace.numel() * 4,
+                               _stream(stream, dev))
+    _raise(st, "mamba2_scan_bwd")
+    res = dict(out)
+    if debug:
+        res.update(d_a=d_a, d_b=d_b, d_c=d_c)
+    return res
+
+
+def bwd_partials(h_history, h_s2, saved, d_context, workspace, *, debug=False, stream=None):
+    """Phase 1 of bwd: writes the split-K partial slices into `workspace`."""
+    B, K, SH2, D, dev = _bwd_args(h_history, h_s2, saved, d_context)
+    _check(workspace, "workspace", None, dev)
+    d_a, d_b, d_c = _debug_bufs(debug, B, K, D, dev)
+    st = lib().mamba2_scan_bwd_partials(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(saved),
+                                        saved.numel() * 4, _ptr(d_context), _ptr(d_a), _ptr(d_b), _ptr(d_c),
+                                        _ptr(workspace), workspace.numel() * 4, _stream(stream, dev))
+    _raise(st, "mamba2_scan_bwd_partials")
+    return dict(d_a=d_a, d_b=d_b, d_c=d_c) if debug else {}
+
+
+def bwd_reduce(B, K, SH2, D, workspace, dW_A, dW_B, dW_C, *, stream=None):
+    """Phase 2 of bwd: fixed-order sum of the slices into dW_A, dW_B, dW_C."""
+    dev = workspace.device
+    _check(workspace, "workspace", None, dev)
+    for name, t in (("dW_A", dW_A), ("dW_B", dW_B), ("dW_C", dW_C)):
+        _check(t, name, (SH2, D), dev)
+    st = lib().mamba2_scan_bwd_reduce(B, K, SH2, D, _ptr(workspace), workspace.numel() * 4, _ptr(dW_A),
+                                      _ptr(dW_B), _ptr(dW_C), _stream(stream, dev))
+    _raise(st, "mamba2_scan_bwd_reduce")

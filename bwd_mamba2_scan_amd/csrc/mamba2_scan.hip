@@ -1,0 +1,605 @@
+// Mamba2 temporal scan, forward and backward, hand-written for gfx950 (MI355X).
+//
+// What is computed (foxhunt "Custom Kernel Optimization Implementation Plan",
+// Tasks 1-2; design spec "cuBLAS Projections + Batch-Parallel Scans", Design
+// section 1): the projections a = H W_A, b = H W_B, c = h_s2 W_C, the gated
+// recurrence x_{t+1} = sigmoid(a_t) x_t + b_t from x_0 = 0, context = c * x_K,
+// and for L = sum(d_context * context) the weight gradients
+// dW_A = H^T d_a, dW_B = H^T d_b, dW_C = h_s2^T d_c.
+//
+// Design (the pages' cuBLAS-plus-scan split is prior art, not followed):
+//
+//  * fwd_kernel: one work-group per (block of 16 samples, group of 16 states).
+//    The [W_A | W_B | W_C] slab of the state group sits in LDS in the fp32
+//    MFMA B-operand layout.  Each of the 8 waves projects one history step of
+//    the 16 samples with v_mfma_f32_16x16x4_f32 (M = samples, N = states,
+//    K = trunk features), streaming every h_history row from HBM once.  The
+//    a|b tiles meet in LDS, where 4 waves run the recurrence, one lane per
+//    (sample, state), in registers.  The readout c is split over the waves by
+//    trunk chunk and summed in a fixed order.
+//
+//  * The backward needs no sequential scan.  With P_t = prod_{v>t} g_v,
+//      d_b_t = d_context * (c P_t),   d_a_t = d_context * (c P_t x_t g_t (1-g_t)),
+//      d_c   = d_context * x_K,
+//    so the forward stores beta_t = c P_t, alpha_t = beta_t x_t g_t (1-g_t)
+//    and x_K ("saved"), and the backward only scales them by d_context.
+//
+//  * bwd_partials_kernel: split-K tall reduction.  One work-group per
+//    (64-feature column block, state group, range of sample blocks); its 8
+//    waves take (sample block, history step) units round-robin and accumulate
+//    H^T [d_a | d_b] and h_s2^T d_c with MFMA (M = features, N = states,
+//    K = rows) in registers.  The waves' partials are summed in LDS in a fixed
+//    order and written as one slice.  Work-groups that share rows are placed
+//    on the same XCD (dispatch is round-robin over the 8 XCDs) so the shared
+//    saved/d_context reads hit that XCD's L2.
+//
+//  * bwd_reduce_kernel: sums the slices in a fixed order, overwriting dW.
+//    No floating-point atomics anywhere, so results are bitwise reproducible.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mamba2_scan.h"
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kGroup = 16;       // states per state group (MFMA N)
+constexpr int kBlock = 16;       // samples per block (MFMA M in the forward)
+constexpr int kPlane = kBlock * kGroup;  // floats in one (sample, state) plane
+constexpr int kColBlock = 64;    // trunk features per backward column block
+constexpr int kFwdWaves = 8;
+constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
+constexpr int kBwdWaves = 8;
+constexpr int kBwdTargetGroups = 256;  // backward work-groups to aim for (one per CU)
+constexpr int kRedThreads = 256;
+constexpr int kRedElems = 64;      // output elements per reduce work-group
+
+__device__ __forceinline__ v4f mfma16x16x4(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f ld4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
+
+// Index of (sample smp in 0..15, state n in 0..15) inside a saved plane.  The
+// backward lane (quad kg, state n) reads samples 4kg..4kg+3 as one float4.
+__device__ __forceinline__ int plane_index(int smp, int n) { return (smp >> 2) * 64 + n * 4 + (smp & 3); }
+
+// ---------------------------------------------------------------------------
+// Forward.
+//   grid  = 8 * NG * ceil(NB / 8) work-groups, 512 threads each.
+//   LDS   = 3 * SH2 * 16 * 4 B (weights) + 16 KiB (a|b exchange) + 8 KiB (c).
+// Work-group w runs on XCD w % 8; the NG state groups of one sample block are
+// given consecutive rounds on the same XCD so their h_history reads share L2.
+template <int NKC>  // SH2 / 16 trunk chunks
+__global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
+    int B, int K, int NG, int NB,
+    const float* __restrict__ H, const float* __restrict__ hs2,
+    const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
+    float* __restrict__ ctx, float* __restrict__ saved) {
+  constexpr int SH2 = NKC * 16;
+  __shared__ v4f sWa[NKC * 64];
+  __shared__ v4f sWb[NKC * 64];
+  __shared__ v4f sWc[NKC * 64];
+  __shared__ float sXa[kChunk][kPlane];
+  __shared__ float sXb[kChunk][kPlane];
+  __shared__ float sC[kFwdWaves][kPlane];
+
+  const int D = NG * kGroup;
+  const int xcd = blockIdx.x & 7;
+  const int round = blockIdx.x >> 3;
+  const int sg = round % NG;
+  const int blk = (round / NG) * 8 + xcd;
+  if (blk >= NB) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int kg = lane >> 4;  // k-group of the A/B operands, row quad of the result
+  const int m = lane & 15;   // row of A (sample) / column of B and result (state)
+
+  // Weight slab in B-operand layout: entry (kc, lane) holds
+  // W[kc*16 + 4*(lane>>4) + i][sg*16 + (lane&15)] for i = 0..3.
+  for (int e = tid; e < NKC * 64; e += kFwdWaves * 64) {
+    const int kc = e >> 6, l = e & 63;
+    const int j0 = kc * 16 + 4 * (l >> 4);
+    const int s = sg * kGroup + (l & 15);
+    v4f a, b, c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = WA[(size_t)(j0 + i) * D + s];
+      b[i] = WB[(size_t)(j0 + i) * D + s];
+      c[i] = WC[(size_t)(j0 + i) * D + s];
+    }
+    sWa[e] = a;
+    sWb[e] = b;
+    sWc[e] = c;
+  }
+  __syncthreads();
+
+  // A-operand row of this lane: sample blk*16 + m, clamped into range (rows of
+  // samples >= B are computed but never stored and never reach a gradient).
+  const int smp_a = min(blk * kBlock + m, B - 1);
+
+  // Readout c: wave w takes trunk chunks kc = w, w+8, ...
+  {
+    const float* hrow = hs2 + (size_t)smp_a * SH2 + 4 * kg;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      if ((kc & (kFwdWaves - 1)) != wave) continue;
+      const v4f av = ld4(hrow + kc * 16);
+      const v4f bv = sWc[kc * 64 + lane];
+      acc = mfma16x16x4(av[0], bv[0], acc);
+      acc = mfma16x16x4(av[1], bv[1], acc);
+      acc = mfma16x16x4(av[2], bv[2], acc);
+      acc = mfma16x16x4(av[3], bv[3], acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sC[wave][(4 * kg + r) * kGroup + m] = acc[r];
+  }
+
+  // Scan lanes: waves 0..3, lane (i = lane>>4, n = lane&15) owns sample
+  // smp = 4*wave + i and state n.
+  const bool scanner = wave < 4;
+  const int smp = 4 * wave + kg;
+  const int pidx = plane_index(smp & 15, m);
+  const size_t blk_stride = (size_t)(2 * K + 1) * kPlane;
+  float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
+  float x = 0.f, c = 0.f;
+  float G[kChunk], U[kChunk];
+
+  const int nchunks = (K + kChunk - 1) / kChunk;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int t = ch * kChunk + wave;
+    if (t < K) {
+      const float* hrow = H + ((size_t)smp_a * K + t) * SH2 + 4 * kg;
+      v4f hv[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) hv[kc] = ld4(hrow + kc * 16);
+      v4f acca = {0.f, 0.f, 0.f, 0.f};
+      v4f accb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const v4f wa = sWa[kc * 64 + lane];
+        const v4f wb = sWb[kc * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acca = mfma16x16x4(hv[kc][i], wa[i], acca);
+          accb = mfma16x16x4(hv[kc][i], wb[i], accb);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sXa[wave][(4 * kg + r) * kGroup + m] = acca[r];
+        sXb[wave][(4 * kg + r) * kGroup + m] = accb[r];
+      }
+    }
+    __syncthreads();
+
+    if (scanner) {
+      const int idx = smp * kGroup + m;
+      if (ch == 0) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kFwdWaves; ++w) s += sC[w][idx];
+        c = s;
+      }
+      const int tn = min(kChunk, K - ch * kChunk);
+#pragma unroll
+      for (int tt = 0; tt < kChunk; ++tt) {
+        if (tt < tn) {
+          const float a = sXa[tt][idx];
+          const float b = sXb[tt][idx];
+          const float e = expf(-a);
+          const float g = 1.f / (1.f + e);
+          // 1 - g, computed without cancellation: e*g = e/(1+e) for a > 0.
+          const float omg = a > 0.f ? e * g : 1.f - g;
+          U[tt] = x * g * omg;
+          G[tt] = g;
+          x = g * x + b;
+        }
+      }
+      if (ch + 1 < nchunks) {
+        // Park g_t and u_t in the alpha/beta slots; the reverse pass below
+        // reads them back (same thread) and overwrites them.
+#pragma unroll
+        for (int tt = 0; tt < kChunk; ++tt) {
+          const int tg = ch * kChunk + tt;
+          sv[(size_t)(2 * tg) * kPlane + pidx] = G[tt];
+          sv[(size_t)(2 * tg + 1) * kPlane + pidx] = U[tt];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!scanner) return;
+
+  const int b_glob = blk * kBlock + smp;
+  if (b_glob < B) ctx[(size_t)b_glob * D + sg * kGroup + m] = c * x;
+  sv[(size_t)(2 * K) * kPlane + pidx] = x;
+
+  // Reverse pass: P = c * prod_{v>t} g_v, beta_t = P, alpha_t = P * u_t.
+  float P = c;
+  {
+    const int ch = nchunks - 1;
+    const int tn = K - ch * kChunk;
+#pragma unroll
+    for (int tt = kChunk - 1; tt >= 0; --tt) {
+      if (tt < tn) {
+        const int tg = ch * kChunk + tt;
+        sv[(size_t)(2 * tg) * kPlane + pidx] = P * U[tt];
+        sv[(size_t)(2 * tg + 1) * kPlane + pidx] = P;
+        P *= G[tt];
+      }
+    }
+  }
+  for (int tg = (nchunks - 1) * kChunk - 1; tg >= 0; --tg) {
+    float* pa = sv + (size_t)(2 * tg) * kPlane + pidx;
+    float* pb = sv + (size_t)(2 * tg + 1) * kPlane + pidx;
+    const float g = *pa;
+    const float u = *pb;
+    *pa = P * u;
+    *pb = P;
+    P *= g;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, phase 1: split-K partial products.
+//   grid = 8 * V * ceil(P / 8), V = (SH2/64) * NG variants, 512 threads.
+// Work-group w: XCD w % 8, variant v = (w/8) % V (column block jb, state
+// group sg), slice p = ((w/8) / V) * 8 + w % 8 covering sample blocks
+// [p*BPW, min(NB, (p+1)*BPW)).
+//
+// MFMA roles (v_mfma_f32_16x16x4_f32, D[M=16][N=16] += A[16][4] B[4][16]):
+//   M = features jb*64 + 4*row + q (four M tiles q share one float4 load),
+//   N = states sg*16 + n, K = the 4 samples 4*kg + i of step i.
+//   A lane (kg, m): H[sample 4kg+i][t][jb*64 + 4m + q]
+//   B lane (kg, n): d_x[sample 4kg+i][t][n]
+__global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
+    int B, int K, int SH2, int NG, int NB, int P, int BPW,
+    const float* __restrict__ H, const float* __restrict__ hs2,
+    const float* __restrict__ saved, const float* __restrict__ dctx,
+    float* __restrict__ d_a_out, float* __restrict__ d_b_out, float* __restrict__ d_c_out,
+    float* __restrict__ ws) {
+  __shared__ float sRed[kBwdWaves][3 * kColBlock * kGroup];
+
+  const int NJB = SH2 / kColBlock;
+  const int V = NJB * NG;
+  const int xcd = blockIdx.x & 7;
+  const int round = blockIdx.x >> 3;
+  const int v = round % V;
+  const int p = (round / V) * 8 + xcd;
+  if (p >= P) return;
+  const int jb = v % NJB;
+  const int sg = v / NJB;
+  const int D = NG * kGroup;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int kg = lane >> 4;
+  const int m = lane & 15;
+  const bool write_dbg = (jb == 0);
+
+  const int blk0 = p * BPW;
+  const int nblk = min(NB - blk0, BPW);
+  const size_t blk_stride = (size_t)(2 * K + 1) * kPlane;
+  const int col = jb * kColBlock + 4 * m;
+  const int state = sg * kGroup + m;
+
+  v4f acc[4][3];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) acc[q][pl] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int nunits = nblk * K;
+  for (int u = wave; u < nunits; u += kBwdWaves) {
+    const int blk = blk0 + u / K;
+    const int t = u - (u / K) * K;
+    const int sbase = blk * kBlock + 4 * kg;
+    const float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
+    const v4f al = ld4(sv + (size_t)(2 * t) * kPlane + 4 * lane);
+    const v4f be = ld4(sv + (size_t)(2 * t + 1) * kPlane + 4 * lane);
+    v4f hv[4];
+    float da[4], db[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = sbase + i;
+      const bool ok = s < B;
+      const int sc = ok ? s : B - 1;
+      const float dc = ok ? dctx[(size_t)sc * D + state] : 0.f;
+      da[i] = dc * al[i];
+      db[i] = dc * be[i];
+      const v4f h = ld4(H + ((size_t)sc * K + t) * SH2 + col);
+      hv[i] = ok ? h : v4f{0.f, 0.f, 0.f, 0.f};
+      if (write_dbg && ok) {
+        if (d_a_out) d_a_out[((size_t)s * K + t) * D + state] = da[i];
+        if (d_b_out) d_b_out[((size_t)s * K + t) * D + state] = db[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q][0] = mfma16x16x4(hv[i][q], da[i], acc[q][0]);
+        acc[q][1] = mfma16x16x4(hv[i][q], db[i], acc[q][1]);
+      }
+    }
+  }
+
+  // dW_C: wave w takes the slice's sample blocks w, w+8, ...
+  for (int bi = wave; bi < nblk; bi += kBwdWaves) {
+    const int blk = blk0 + bi;
+    const int sbase = blk * kBlock + 4 * kg;
+    const float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
+    const v4f xk = ld4(sv + (size_t)(2 * K) * kPlane + 4 * lane);
+    v4f hv[4];
+    float dcc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = sbase + i;
+      const bool ok = s < B;
+      const int sc = ok ? s : B - 1;
+      const float dc = ok ? dctx[(size_t)sc * D + state] : 0.f;
+      dcc[i] = dc * xk[i];
+      const v4f h = ld4(hs2 + (size_t)sc * SH2 + col);
+      hv[i] = ok ? h : v4f{0.f, 0.f, 0.f, 0.f};
+      if (write_dbg && ok && d_c_out) d_c_out[(size_t)s * D + state] = dcc[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q][2] = mfma16x16x4(hv[i][q], dcc[i], acc[q][2]);
+  }
+
+  // Result lane (g = kg, n = m), element r of tile q: feature row
+  // jl = 16*g + 4*r + q of the column block, state n.
+#pragma unroll
+  for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sRed[wave][pl * (kColBlock * kGroup) + (16 * kg + 4 * r + q) * kGroup + m] = acc[q][pl][r];
+  __syncthreads();
+
+  // Slice layout: ws[sg][p][jb][plane][jl][n].
+  float* out = ws + ((size_t)sg * P + p) * ((size_t)SH2 * 3 * kGroup) + (size_t)jb * (3 * kColBlock * kGroup);
+  for (int e = tid; e < 3 * kColBlock * kGroup; e += kBwdWaves * 64) {
+    float s = sRed[0][e];
+#pragma unroll
+    for (int w = 1; w < kBwdWaves; ++w) s += sRed[w][e];
+    out[e] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, phase 2: dW = sum over slices p = 0..P-1, in a fixed order.
+//   grid = ceil(NG * SH2 * 48 / 64), 256 threads: 64 elements x 4 quarters of
+//   the slice range; quarters are combined in order 0..3.
+__global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
+    int SH2, int NG, int P, const float* __restrict__ ws,
+    float* __restrict__ dWA, float* __restrict__ dWB, float* __restrict__ dWC) {
+  __shared__ float sPart[4][kRedElems];
+  const int per_sg = SH2 * 3 * kGroup;
+  const int total = NG * per_sg;
+  const int el = threadIdx.x & (kRedElems - 1);
+  const int qtr = threadIdx.x / kRedElems;
+  const int e = blockIdx.x * kRedElems + el;
+  const bool ok = e < total;
+  const int sg = ok ? e / per_sg : 0;
+  const int o = ok ? e - sg * per_sg : 0;
+
+  const int pq = (P + 3) / 4;
+  const int p0 = qtr * pq;
+  const int p1 = min(P, p0 + pq);
+  float s = 0.f;
+  if (ok) {
+    const float* src = ws + (size_t)sg * P * per_sg + o;
+    for (int p = p0; p < p1; ++p) s += src[(size_t)p * per_sg];
+  }
+  sPart[qtr][el] = s;
+  __syncthreads();
+  if (qtr != 0 || !ok) return;
+  const float tot = ((sPart[0][el] + sPart[1][el]) + sPart[2][el]) + sPart[3][el];
+
+  const int jb = o / (3 * kColBlock * kGroup);
+  const int rem = o - jb * (3 * kColBlock * kGroup);
+  const int pl = rem / (kColBlock * kGroup);
+  const int rem2 = rem - pl * (kColBlock * kGroup);
+  const int jl = rem2 / kGroup;
+  const int n = rem2 - jl * kGroup;
+  const int D = NG * kGroup;
+  float* dst = pl == 0 ? dWA : (pl == 1 ? dWB : dWC);
+  dst[(size_t)(jb * kColBlock + jl) * D + sg * kGroup + n] = tot;
+}
+
+// ---------------------------------------------------------------------------
+// Host side: shape checks and launch plans.
+struct Plan {
+  int B, K, SH2, D, NG, NB, NJB, V;
+  int P, BPW;
+  size_t saved_bytes, ws_bytes;
+};
+
+int make_plan(int B, int K, int SH2, int D, Plan* pl) {
+  if (B <= 0 || K <= 0 || SH2 <= 0 || D <= 0) return MAMBA2_SCAN_EBADDIM;
+  if (D != 16 && D != 32 && D != 64) return MAMBA2_SCAN_EUNSUPPORTED;
+  if (SH2 % kColBlock != 0 || SH2 > 512) return MAMBA2_SCAN_EUNSUPPORTED;
+  // Every element offset must fit comfortably in 64 bits and every block and
+  // unit count in 32 bits.
+  const long long rows = (long long)B * K;
+  if (rows > (1LL << 40) / SH2) return MAMBA2_SCAN_EBADDIM;
+  pl->B = B;
+  pl->K = K;
+  pl->SH2 = SH2;
+  pl->D = D;
+  pl->NG = D / kGroup;
+  pl->NB = (B + kBlock - 1) / kBlock;
+  if ((long long)pl->NB * K > (1LL << 30)) return MAMBA2_SCAN_EBADDIM;
+  pl->NJB = SH2 / kColBlock;
+  pl->V = pl->NJB * pl->NG;
+  int p0 = (kBwdTargetGroups + pl->V - 1) / pl->V;
+  if (p0 > pl->NB) p0 = pl->NB;
+  pl->BPW = (pl->NB + p0 - 1) / p0;
+  pl->P = (pl->NB + pl->BPW - 1) / pl->BPW;
+  pl->saved_bytes = (size_t)pl->NB * pl->NG * (size_t)(2 * K + 1) * kPlane * sizeof(float);
+  pl->ws_bytes = (size_t)pl->NG * pl->P * (size_t)SH2 * 3 * kGroup * sizeof(float);
+  return MAMBA2_SCAN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? MAMBA2_SCAN_OK : MAMBA2_SCAN_EHIP;
+}
+
+template <int NKC>
+void launch_fwd(const Plan& pl, const float* H, const float* hs2, const float* WA, const float* WB,
+                const float* WC, float* ctx, float* saved, hipStream_t st) {
+  const int grid = 8 * pl.NG * ((pl.NB + 7) / 8);
+  hipLaunchKernelGGL(fwd_kernel<NKC>, dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
+                     hs2, WA, WB, WC, ctx, saved);
+}
+
+int check_bwd_common(const Plan& pl, const float* H, const float* hs2, const void* saved, size_t saved_bytes,
+                     const float* dctx, const float* da, const float* db, const float* dc, const void* ws,
+                     size_t ws_bytes) {
+  if (!H || !hs2 || !saved || !dctx || !ws) return MAMBA2_SCAN_ENULL;
+  if (saved_bytes < pl.saved_bytes || ws_bytes < pl.ws_bytes) return MAMBA2_SCAN_ESIZE;
+  if (!aligned16(H) || !aligned16(hs2) || !aligned16(saved) || !aligned16(ws) || !aligned4(dctx))
+    return MAMBA2_SCAN_EALIGN;
+  if ((da && !aligned4(da)) || (db && !aligned4(db)) || (dc && !aligned4(dc))) return MAMBA2_SCAN_EALIGN;
+  return MAMBA2_SCAN_OK;
+}
+
+int check_reduce(const Plan& pl, const void* ws, size_t ws_bytes, const float* dWA, const float* dWB,
+                 const float* dWC) {
+  if (!ws || !dWA || !dWB || !dWC) return MAMBA2_SCAN_ENULL;
+  if (ws_bytes < pl.ws_bytes) return MAMBA2_SCAN_ESIZE;
+  if (!aligned16(ws) || !aligned4(dWA) || !aligned4(dWB) || !aligned4(dWC)) return MAMBA2_SCAN_EALIGN;
+  return MAMBA2_SCAN_OK;
+}
+
+void launch_partials(const Plan& pl, const float* H, const float* hs2, const void* saved, const float* dctx,
+                     float* da, float* db, float* dc, void* ws, hipStream_t st) {
+  const int grid = 8 * pl.V * ((pl.P + 7) / 8);
+  hipLaunchKernelGGL(bwd_partials_kernel, dim3(grid), dim3(kBwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
+                     pl.NB, pl.P, pl.BPW, H, hs2, static_cast<const float*>(saved), dctx, da, db, dc,
+                     static_cast<float*>(ws));
+}
+
+void launch_reduce(const Plan& pl, const void* ws, float* dWA, float* dWB, float* dWC, hipStream_t st) {
+  const int total = pl.NG * pl.SH2 * 3 * kGroup;
+  const int grid = (total + kRedElems - 1) / kRedElems;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, st, pl.SH2, pl.NG, pl.P,
+                     static_cast<const float*>(ws), dWA, dWB, dWC);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mamba2_scan_saved_bytes(int B, int K, int SH2, int STATE_D) {
+  Plan pl;
+  return make_plan(B, K, SH2, STATE_D, &pl) == MAMBA2_SCAN_OK ? pl.saved_bytes : 0;
+}
+
+size_t mamba2_scan_bwd_workspace_bytes(int B, int K, int SH2, int STATE_D) {
+  Plan pl;
+  return make_plan(B, K, SH2, STATE_D, &pl) == MAMBA2_SCAN_OK ? pl.ws_bytes : 0;
+}
+
+int mamba2_scan_fwd(int B, int K, int SH2, int STATE_D, const float* h_history, const float* h_s2,
+                    const float* W_A, const float* W_B, const float* W_C, float* context, void* saved,
+                    size_t saved_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  if (!h_history || !h_s2 || !W_A || !W_B || !W_C || !context || !saved) return MAMBA2_SCAN_ENULL;
+  if (saved_bytes < pl.saved_bytes) return MAMBA2_SCAN_ESIZE;
+  if (!aligned16(h_history) || !aligned16(h_s2) || !aligned16(saved) || !aligned4(W_A) || !aligned4(W_B) ||
+      !aligned4(W_C) || !aligned4(context))
+    return MAMBA2_SCAN_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* sv = static_cast<float*>(saved);
+  switch (SH2 / 64) {
+    case 1: launch_fwd<4>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
+    case 2: launch_fwd<8>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
+    case 3: launch_fwd<12>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
+    case 4: launch_fwd<16>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
+    case 5: launch_fwd<20>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
+    case 6: launch_fwd<24>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
+    case 7: launch_fwd<28>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
+    case 8: launch_fwd<32>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
+    default: return MAMBA2_SCAN_EUNSUPPORTED;
+  }
+  return launch_status();
+}
+
+int mamba2_scan_bwd_partials(int B, int K, int SH2, int STATE_D, const float* h_history, const float* h_s2,
+                             const void* saved, size_t saved_bytes, const float* d_context, float* d_a, float* d_b,
+                             float* d_c, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_bwd_common(pl, h_history, h_s2, saved, saved_bytes, d_context, d_a, d_b, d_c, workspace,
+                        workspace_bytes);
+  if (st != MAMBA2_SCAN_OK) return st;
+  launch_partials(pl, h_history, h_s2, saved, d_context, d_a, d_b, d_c, workspace,
+                  static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int mamba2_scan_bwd_reduce(int B, int K, int SH2, int STATE_D, const void* workspace, size_t workspace_bytes,
+                           float* dW_A, float* dW_B, float* dW_C, void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_reduce(pl, workspace, workspace_bytes, dW_A, dW_B, dW_C);
+  if (st != MAMBA2_SCAN_OK) return st;
+  launch_reduce(pl, workspace, dW_A, dW_B, dW_C, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int mamba2_scan_bwd(int B, int K, int SH2, int STATE_D, const float* h_history, const float* h_s2,
+                    const void* saved, size_t saved_bytes, const float* d_context, float* dW_A, float* dW_B,
+                    float* dW_C, float* d_a, float* d_b, float* d_c, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_bwd_common(pl, h_history, h_s2, saved, saved_bytes, d_context, d_a, d_b, d_c, workspace,
+                        workspace_bytes);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_reduce(pl, workspace, workspace_bytes, dW_A, dW_B, dW_C);
+  if (st != MAMBA2_SCAN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_partials(pl, h_history, h_s2, saved, d_context, d_a, d_b, d_c, workspace, s);
+  st = launch_status();
+  if (st != MAMBA2_SCAN_OK) return st;
+  launch_reduce(pl, workspace, dW_A, dW_B, dW_C, s);
+  return launch_status();
+}
+
+const char* mamba2_scan_strerror(int status) {
+  switch (status) {
+    case MAMBA2_SCAN_OK: return "success";
+    case MAMBA2_SCAN_EBADDIM: return "invalid dimension (must be > 0 and sizes must not overflow)";
+    case MAMBA2_SCAN_EUNSUPPORTED: return "unsupported shape (STATE_D in {16,32,64}; SH2 % 64 == 0, SH2 <= 512)";
+    case MAMBA2_SCAN_ENULL: return "a required pointer is NULL";
+    case MAMBA2_SCAN_ESIZE: return "saved or workspace buffer is smaller than required";
+    case MAMBA2_SCAN_EALIGN: return "pointer misaligned (h_history, h_s2, saved, workspace need 16 bytes)";
+    case MAMBA2_SCAN_EHIP: return "HIP runtime error while enqueuing a kernel";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+/*
+ * mamba2_scan.h -- C ABI of the Mamba2 temporal scan (forward and backward)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (foxhunt "Custom Kernel Optimization Implementation Plan",
+ * Task 1 "Mamba2 Forward" and Task 2 "Mamba2 Backward"; design spec
+ * "cuBLAS Projections + Batch-Parallel Scans", Design section 1):
+ *
+ *   a = H W_A,  b = H W_B   over the B*K history rows H = h_history[B][K][SH2]
+ *   c = h_s2 W_C            over the B current trunk rows h_s2[B][SH2]
+ *   x_0 = 0,  x_{t+1} = sigmoid(a_t) * x_t + b_t   for t = 0 .. K-1
+ *   context[b][s] = c[b][s] * x_K[b][s]
+ *
+ * and, for the scalar L = sum_{b,s} d_context[b][s] * context[b][s],
+ *
+ *   dW_A = H^T d_a,  dW_B = H^T d_b,  dW_C = h_s2^T d_c
+ *
+ * where d_a, d_b, d_c are dL/da, dL/db, dL/dc (reverse scan).
+ *
+ * Conventions for every entry point:
+ *   - All tensors are fp32, row-major and contiguous.  Element (b, t, j) of
+ *     h_history is at (b*K + t)*SH2 + j; W_X[j][s] is at j*STATE_D + s;
+ *     context and d_context [b][s] at b*STATE_D + s.  Row t = K-1 is the
+ *     newest history step.
+ *   - Every pointer is device memory owned by the caller.  The library
+ *     allocates nothing, keeps no state between calls and never synchronises:
+ *     work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Supported shapes: B >= 1, K >= 1, STATE_D in {16, 32, 64},
+ *     SH2 a multiple of 64 with 64 <= SH2 <= 512.
+ *   - h_history, h_s2, saved and workspace must be 16-byte aligned; the other
+ *     pointers 4-byte aligned.
+ *   - Every argument check runs before any work is enqueued.  On a nonzero
+ *     return nothing has been written, except after MAMBA2_SCAN_EHIP.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Calls on different streams may run concurrently if their output and
+ *     scratch buffers do not overlap.
+ */
+#ifndef MAMBA2_SCAN_H
+#define MAMBA2_SCAN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MAMBA2_SCAN_OK            0
+#define MAMBA2_SCAN_EBADDIM      -1 /* a dimension <= 0, or sizes overflow    */
+#define MAMBA2_SCAN_EUNSUPPORTED -2 /* STATE_D or SH2 outside the list above  */
+#define MAMBA2_SCAN_ENULL        -3 /* a required pointer is NULL             */
+#define MAMBA2_SCAN_ESIZE        -4 /* saved or workspace buffer too small    */
+#define MAMBA2_SCAN_EALIGN       -5 /* a pointer is not aligned as required   */
+#define MAMBA2_SCAN_EHIP         -6 /* the HIP runtime refused a launch       */
+
+/*
+ * Bytes of the `saved` buffer that mamba2_scan_fwd fills and mamba2_scan_bwd
+ * reads for these dimensions (the plan's Task 2 reuses the forward's
+ * projections instead of recomputing them).  Its contents are private to the
+ * library.  Returns 0 if the dimensions are invalid or unsupported.
+ */
+size_t mamba2_scan_saved_bytes(int B, int K, int SH2, int STATE_D);
+
+/*
+ * Bytes of the scratch workspace mamba2_scan_bwd needs: the split-K partial
+ * sums of the weight gradients, one slice per backward work-group.  The
+ * number of slices depends only on the dimensions, so the reduction order,
+ * and with it every bit of dW, is the same on every call.  Returns 0 if the
+ * dimensions are invalid or unsupported.
+ */
+size_t mamba2_scan_bwd_workspace_bytes(int B, int K, int SH2, int STATE_D);
+
+/*
+ * Forward (plan Task 1; design spec forward steps 1-2).
+ *   h_history [B][K][SH2], h_s2 [B][SH2], W_A/W_B/W_C [SH2][STATE_D]  (in)
+ *   context   [B][STATE_D]                                            (out)
+ *   saved     saved_bytes >= mamba2_scan_saved_bytes(...)             (out)
+ * `saved` receives what the backward needs (per-step gate terms and x_K);
+ * pass it unchanged to mamba2_scan_bwd with the same inputs.
+ */
+int mamba2_scan_fwd(int B, int K, int SH2, int STATE_D,
+                    const float* h_history, const float* h_s2,
+                    const float* W_A, const float* W_B, const float* W_C,
+                    float* context, void* saved, size_t saved_bytes,
+                    void* stream);
+
+/*
+ * Backward (plan Task 2; design spec backward steps 1-3).
+ *   h_history, h_s2       the same buffers the forward read           (in)
+ *   saved                 the forward's `saved` for those inputs      (in)
+ *   d_context [B][STATE_D] upstream gradient dL/dcontext              (in)
+ *   dW_A, dW_B, dW_C [SH2][STATE_D]                                   (out)
+ *   d_a, d_b [B][K][STATE_D], d_c [B][STATE_D]  optional (out); NULL skips
+ *   workspace             workspace_bytes >= mamba2_scan_bwd_workspace_bytes
+ * Equivalent to mamba2_scan_bwd_partials followed by mamba2_scan_bwd_reduce
+ * on the same stream.  The weight gradients are bitwise reproducible.
+ */
+int mamba2_scan_bwd(int B, int K, int SH2, int STATE_D,
+                    const float* h_history, const float* h_s2,
+                    const void* saved, size_t saved_bytes,
+                    const float* d_context,
+                    float* dW_A, float* dW_B, float* dW_C,
+                    float* d_a, float* d_b, float* d_c,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * First phase of the backward: the reverse scan and the split-K products
+ * H^T [d_a | d_b] and h_s2^T d_c, one partial slice per work-group, written
+ * to `workspace`.  Arguments as for mamba2_scan_bwd.
+ */
+int mamba2_scan_bwd_partials(int B, int K, int SH2, int STATE_D,
+                             const float* h_history, const float* h_s2,
+                             const void* saved, size_t saved_bytes,
+                             const float* d_context,
+                             float* d_a, float* d_b, float* d_c,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * Second phase: sums the partial slices of `workspace` in a fixed order and
+ * overwrites dW_A, dW_B, dW_C [SH2][STATE_D].
+ */
+int mamba2_scan_bwd_reduce(int B, int K, int SH2, int STATE_D,
+                           const void* workspace, size_t workspace_bytes,
+                           float* dW_A, float* dW_B, float* dW_C,
+                           void* stream);
+
+/* Static text for a status code. */
+const char* mamba2_scan_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA2_SCAN_H */

@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes its buffers, and rejects bad arguments before it
+enqueues anything.  Every call below fails an argument check, so no kernel is
+ever launched and no pointer is ever dereferenced.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+import bwd_mamba2_scan_amd as m2
+
+
+@pytest.fixture(scope="module")
+def L():
+    return m2.lib()
+
+
+def test_exports_every_header_symbol(L):
+    names = m2.header_functions()
+    assert set(names) == {
+        "mamba2_scan_saved_bytes", "mamba2_scan_bwd_workspace_bytes", "mamba2_scan_fwd",
+        "mamba2_scan_bwd", "mamba2_scan_bwd_partials", "mamba2_scan_bwd_reduce", "mamba2_scan_strerror",
+    }
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_covers_codes():
+    for code in (m2.OK, m2.EBADDIM, m2.EUNSUPPORTED, m2.ENULL, m2.ESIZE, m2.EALIGN, m2.EHIP):
+        assert m2.strerror(code) and m2.strerror(code) != "unknown status"
+    assert m2.strerror(12345) == "unknown status"
+
+
+def test_buffer_sizes():
+    # saved: per 16-sample block and state group, 2K+1 planes of 16x16 floats
+    for B, K, SH2, D in ((64, 8, 256, 16), (8192, 8, 256, 16), (17, 3, 128, 32), (1, 1, 64, 64)):
+        nb = (B + 15) // 16
+        assert m2.saved_bytes(B, K, SH2, D) == nb * (D // 16) * (2 * K + 1) * 256 * 4
+        ws = m2.workspace_bytes(B, K, SH2, D)
+        assert ws > 0 and ws % (SH2 * 48 * 4 * (D // 16)) == 0
+    # workspace never shrinks as B grows
+    prev = 0
+    for B in list(range(1, 200, 7)) + [1024, 4096, 8192, 32768, 100000]:
+        ws = m2.workspace_bytes(B, 8, 256, 16)
+        assert ws >= prev
+        prev = ws
+    assert m2.workspace_bytes(8192, 8, 256, 16) == 64 * 256 * 48 * 4
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((0, 8, 256, 16), m2.EBADDIM), ((8, 0, 256, 16), m2.EBADDIM), ((8, 8, 0, 16), m2.EBADDIM),
+    ((8, 8, 256, 0), m2.EBADDIM), ((-1, 8, 256, 16), m2.EBADDIM),
+    ((8, 8, 256, 8), m2.EUNSUPPORTED), ((8, 8, 256, 48), m2.EUNSUPPORTED),
+    ((8, 8, 100, 16), m2.EUNSUPPORTED), ((8, 8, 1024, 16), m2.EUNSUPPORTED),
+    ((2 ** 30, 2 ** 10, 512, 16), m2.EBADDIM),
+])
+def test_bad_dims(L, dims, code):
+    assert m2.saved_bytes(*dims) == 0
+    assert m2.workspace_bytes(*dims) == 0
+    fake = ctypes.c_void_p(0x10000)
+    assert L.mamba2_scan_fwd(*dims, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None) == code
+    assert L.mamba2_scan_bwd(*dims, fake, fake, fake, 1 << 40, fake, fake, fake, fake, None, None, None,
+                             fake, 1 << 40, None) == code
+    assert L.mamba2_scan_bwd_partials(*dims, fake, fake, fake, 1 << 40, fake, None, None, None,
+                                      fake, 1 << 40, None) == code
+    assert L.mamba2_scan_bwd_reduce(*dims, fake, 1 << 40, fake, fake, fake, None) == code
+
+
+def _fwd_args(dims, ptrs, saved_bytes):
+    return (*dims, *ptrs, saved_bytes, None)
+
+
+def test_fwd_argument_checks(L):
+    dims = (64, 8, 256, 16)
+    need = m2.saved_bytes(*dims)
+    good = ctypes.c_void_p(0x10000)
+    # a NULL in any required slot
+    for i in range(7):
+        ptrs = [good] * 7
+        ptrs[i] = None
+        assert L.mamba2_scan_fwd(*_fwd_args(dims, ptrs, need)) == m2.ENULL, i
+    # saved too small
+    assert L.mamba2_scan_fwd(*_fwd_args(dims, [good] * 7, need - 4)) == m2.ESIZE
+    # misaligned: 16 bytes for h_history, h_s2, saved (slots 0, 1, 6); 4 for the rest
+    for i, off in ((0, 4), (1, 8), (6, 12), (2, 2), (5, 1)):
+        ptrs = [good] * 7
+        ptrs[i] = ctypes.c_void_p(0x10000 + off)
+        assert L.mamba2_scan_fwd(*_fwd_args(dims, ptrs, need)) == m2.EALIGN, i
+
+
+def test_bwd_argument_checks(L):
+    dims = (100, 5, 192, 32)
+    sv = m2.saved_bytes(*dims)
+    ws = m2.workspace_bytes(*dims)
+    g = ctypes.c_void_p(0x20000)
+
+    def call(h=g, hs=g, saved=g, svb=sv, dctx=g, dwa=g, dwb=g, dwc=g, da=None, db=None, dc=None, w=g, wsb=ws):
+        return L.mamba2_scan_bwd(*dims, h, hs, saved, svb, dctx, dwa, dwb, dwc, da, db, dc, w, wsb, None)
+
+    for kw in ("h", "hs", "saved", "dctx", "dwa", "dwb", "dwc", "w"):
+        assert call(**{kw: None}) == m2.ENULL, kw
+    assert call(svb=sv - 1) == m2.ESIZE
+    assert call(wsb=ws - 4) == m2.ESIZE
+    for kw, off in (("h", 4), ("hs", 8), ("saved", 4), ("w", 8), ("dctx", 2), ("dwa", 1), ("da", 2)):
+        assert call(**{kw: ctypes.c_void_p(0x20000 + off)}) == m2.EALIGN, kw
+
+    assert L.mamba2_scan_bwd_partials(*dims, g, g, g, sv, g, None, None, None, None, ws, None) == m2.ENULL
+    assert L.mamba2_scan_bwd_partials(*dims, g, g, g, sv, g, None, None, None, g, ws - 4, None) == m2.ESIZE
+    assert L.mamba2_scan_bwd_reduce(*dims, g, ws, None, g, g, None) == m2.ENULL
+    assert L.mamba2_scan_bwd_reduce(*dims, g, ws - 4, g, g, g, None) == m2.ESIZE
+    assert L.mamba2_scan_bwd_reduce(*dims, ctypes.c_void_p(0x20004), ws, g, g, g, None) == m2.EALIGN

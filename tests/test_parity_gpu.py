@@ -1,0 +1,207 @@
+"""Parity of the HIP path against the CPU oracle, on an MI355X.
+
+Tolerances (benchmark spec, restated):
+  * outputs (context, and d_a, d_b, d_c when requested): elementwise
+    |gpu - ref| <= 1e-4 * (1 + |ref|)
+  * weight gradients: sum|gpu - ref| / sum|ref| <= 1e-3 per matrix.
+The GPU computes in fp32 (fp32 MFMA with fp32 accumulation); the oracle in fp64.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import bwd_mamba2_scan_amd as m2
+from oracle import mamba2_oracle as orc
+from tests.inputs import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-4
+DW_TOL = 1e-3
+
+
+def _dev():
+    assert torch.cuda.is_available(), "no GPU visible"
+    return torch.device("cuda:0")
+
+
+def _to_dev(inputs):
+    dev = _dev()
+    return {k: torch.from_numpy(v).to(dev) for k, v in inputs.items()}
+
+
+def run_gpu(t, debug=False):
+    ctx, saved = m2.fwd(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"])
+    g = m2.bwd(t["h_history"], t["h_s2"], saved, t["d_context"], debug=debug)
+    torch.cuda.synchronize()
+    out = {"context": ctx.cpu().numpy()}
+    out.update({k: v.cpu().numpy() for k, v in g.items()})
+    return out
+
+
+def assert_elementwise(gpu, ref, name, tol=OUT_TOL):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{name}: non-finite values"
+    err = np.abs(gpu - ref)
+    bound = tol * (1.0 + np.abs(ref))
+    worst = int(np.argmax(err / bound))
+    assert np.all(err <= bound), (
+        f"{name}: {int(np.sum(err > bound))} of {err.size} elements out of tolerance; worst at flat index "
+        f"{worst}: gpu={gpu.flat[worst]!r} ref={ref.flat[worst]!r}")
+
+
+def assert_l1(gpu, ref, name, tol=DW_TOL):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{name}: non-finite values"
+    den = float(np.sum(np.abs(ref)))
+    rel = float(np.sum(np.abs(gpu - ref))) / den if den > 0 else float(np.sum(np.abs(gpu)))
+    assert rel <= tol, f"{name}: L1 relative error {rel:.3e} > {tol:.1e}"
+
+
+def check_against_oracle(inputs, debug=True):
+    t = _to_dev(inputs)
+    got = run_gpu(t, debug=debug)
+    f, b = orc.fwd_bwd(inputs)
+    assert_elementwise(got["context"], f.context, "context")
+    for name in ("dW_A", "dW_B", "dW_C"):
+        assert_l1(got[name], getattr(b, name), name)
+    if debug:
+        assert_elementwise(got["d_a"], b.d_a, "d_a")
+        assert_elementwise(got["d_b"], b.d_b, "d_b")
+        assert_elementwise(got["d_c"], b.d_c, "d_c")
+    return got, f, b
+
+
+# Shapes chosen to cover: one sample, ragged batches (B % 16 != 0), K = 1,
+# K across the 8-step projection rounds (9, 17, 64), every SH2 multiple of 64
+# from 64 to 512, all three state widths, and partial slices in the backward.
+EDGE_SHAPES = [
+    (1, 1, 64, 16),
+    (1, 8, 256, 16),
+    (17, 3, 128, 16),
+    (33, 9, 256, 16),
+    (5, 17, 192, 32),
+    (40, 8, 320, 64),
+    (16, 8, 512, 64),
+    (100, 2, 448, 16),
+    (64, 64, 256, 16),
+    (3, 8, 384, 32),
+    (250, 5, 64, 64),
+    (129, 1, 512, 32),
+    (300, 12, 256, 16),
+]
+
+
+@pytest.mark.parametrize("B,K,SH2,D", EDGE_SHAPES, ids=lambda v: str(v))
+def test_edge_shapes(B, K, SH2, D):
+    check_against_oracle(make_inputs(B, K, SH2, D, seed=B * 7 + K))
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "pages_shape"])
+def test_workload_full(name):
+    check_against_oracle(workload_inputs(name), debug=(name != "pages_shape"))
+
+
+@pytest.mark.parametrize("name", ["long_history", "wide_state"])
+def test_workload_large(name):
+    got, f, _ = check_against_oracle(workload_inputs(name), debug=False)
+    if name == "long_history":
+        # the +2 logit shift gives long-memory gates
+        assert 0.8 < float(np.mean(f.g)) < 0.95
+
+
+def test_saturated_and_extreme_logits():
+    """Gates pinned at 0 and 1 (|a| up to ~100): finite results, oracle parity."""
+    inp = make_inputs(48, 6, 128, 16, seed=77)
+    inp["h_history"][:, :, 0] = 1.0
+    inp["W_A"][0, :8] = -100.0
+    inp["W_A"][0, 8:] = 100.0
+    check_against_oracle(inp)
+
+
+def test_bitwise_determinism():
+    """Same inputs, same shape -> identical bits for context and every dW."""
+    t = _to_dev(workload_inputs("mid"))
+    r1 = run_gpu(t)
+    r2 = run_gpu(t)
+    for k in ("context", "dW_A", "dW_B", "dW_C"):
+        assert np.array_equal(r1[k].view(np.uint32), r2[k].view(np.uint32)), k
+
+
+def test_split_phase_matches_bwd():
+    """bwd_partials + bwd_reduce gives the same bits as bwd."""
+    inp = make_inputs(200, 8, 256, 32, seed=5)
+    t = _to_dev(inp)
+    B, K, SH2 = inp["h_history"].shape
+    D = inp["W_A"].shape[1]
+    ctx, saved = m2.fwd(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"])
+    one = m2.bwd(t["h_history"], t["h_s2"], saved, t["d_context"])
+    ws = m2.alloc_workspace(B, K, SH2, D, t["h_history"].device)
+    m2.bwd_partials(t["h_history"], t["h_s2"], saved, t["d_context"], ws)
+    outs = [torch.empty((SH2, D), device=ws.device) for _ in range(3)]
+    m2.bwd_reduce(B, K, SH2, D, ws, *outs)
+    torch.cuda.synchronize()
+    for o, k in zip(outs, ("dW_A", "dW_B", "dW_C")):
+        assert torch.equal(o, one[k]), k
+
+
+def test_batch_split_additivity():
+    """dW(all samples) = dW(first part) + dW(rest); context rows do not depend on the split."""
+    inp = make_inputs(160, 8, 256, 16, seed=9)
+    t = _to_dev(inp)
+    full = run_gpu(t)
+    cut = 70
+    parts = []
+    for sl in (slice(0, cut), slice(cut, None)):
+        tp = {k: (v[sl].contiguous() if k in ("h_history", "h_s2", "d_context") else v) for k, v in t.items()}
+        parts.append(run_gpu(tp))
+    np.testing.assert_allclose(np.concatenate([parts[0]["context"], parts[1]["context"]]), full["context"],
+                               rtol=0, atol=0)
+    for k in ("dW_A", "dW_B", "dW_C"):
+        assert_l1(parts[0][k].astype(np.float64) + parts[1][k], full[k].astype(np.float64), k, tol=1e-5)
+
+
+def test_outputs_overwritten_not_accumulated():
+    """Pre-filled output buffers are overwritten (the pages' bias-grad reduce that accumulates is not followed)."""
+    inp = make_inputs(32, 4, 128, 16, seed=3)
+    t = _to_dev(inp)
+    B, K, SH2 = inp["h_history"].shape
+    D = 16
+    ctx = torch.full((B, D), 123.0, device=t["h_s2"].device)
+    ctx, saved = m2.fwd(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], context=ctx)
+    out = {k: torch.full((SH2, D), -7.0, device=ctx.device) for k in ("dW_A", "dW_B", "dW_C")}
+    m2.bwd(t["h_history"], t["h_s2"], saved, t["d_context"], out=out)
+    torch.cuda.synchronize()
+    f, b = orc.fwd_bwd(inp)
+    assert_elementwise(ctx.cpu().numpy(), f.context, "context")
+    for k in ("dW_A", "dW_B", "dW_C"):
+        assert_l1(out[k].cpu().numpy(), getattr(b, k), k)
+
+
+def test_binding_rejects_bad_arguments():
+    dev = _dev()
+    h = torch.zeros((4, 2, 64), device=dev)
+    hs = torch.zeros((4, 64), device=dev)
+    w = torch.zeros((64, 16), device=dev)
+    with pytest.raises(TypeError):
+        m2.fwd(h.double(), hs, w, w, w)
+    with pytest.raises(ValueError):
+        m2.fwd(h, hs[:, :32].contiguous(), w, w, w)
+    with pytest.raises(ValueError):
+        m2.fwd(h, hs, w.t(), w, w)
+    w8 = torch.zeros((64, 8), device=dev)
+    with pytest.raises(ValueError):
+        m2.fwd(h, hs, w8, w8, w8)
+    ctx, saved = m2.fwd(h, hs, w, w, w)
+    with pytest.raises(m2.Mamba2ScanError):
+        m2.bwd(h, hs, saved[:-1], torch.zeros((4, 16), device=dev))
+    torch.cuda.synchronize()
+
+
+def test_workloads_table_matches_pages_shape():
+    w = WORKLOADS["pages_shape"]
+    assert (w.B, w.K, w.SH2, w.D) == (8192, 8, 256, 16)
