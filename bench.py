@@ -12,10 +12,10 @@ and its backward R/2 other steps stream far more than the cache holds.  Each
 step is one captured HIP graph; the K timed steps are graph replays bracketed
 by device synchronisation.
 
-Per-kernel durations come from HIP events around each kernel of a second,
-eagerly launched pass of the same rotation (on the stream the kernels run
-on); the dominant kernel's algorithmic bytes over its mean duration give the
-roofline figure.
+Per-kernel durations come from HIP events (on the stream the kernels run on)
+around a batch of back-to-back launches of one kernel that walks the same
+rotation; the dominant kernel's algorithmic bytes over its mean duration give
+the roofline figure.
 """
 from __future__ import annotations
 
@@ -96,7 +96,7 @@ def cpu_baseline(workload_name, budget_s=12.0):
         t0 = time.perf_counter()
         orc.fwd_bwd(inp)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+        if time.perf_counter() - t_start > budget_s or len(times) >= 1000:
             break
     return {
         "value": round(statistics.median(times) * 1e3, 3),
@@ -236,23 +236,25 @@ def main():
 
     # ---- per-kernel durations: HIP events around each kernel, cold rotation,
     # eager launches on the current stream (the one the kernels run on)
+    # Each kernel is timed over a batch of back-to-back launches that walk the
+    # rotation (so every launch reads a set the previous R-1 launches did not
+    # touch), bracketed by one event pair; the mean per launch is reported.
     names = ("fwd_kernel", "bwd_partials_kernel", "bwd_reduce_kernel")
-    recorded = []
-    for i in range(max(args.steps, 2 * R) + R):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        evs[0].record()
-        fwd(sets[i % R])
-        evs[1].record()
-        sb = sets[(i - R // 2) % R]
-        partials(sb)
-        evs[2].record()
-        reduce(sb)
-        evs[3].record()
-        if i >= R:  # the first rotation is warm-up
-            recorded.append(evs)
-    torch.cuda.synchronize()
-    kern_us = {n: statistics.mean(evs[k].elapsed_time(evs[k + 1]) for evs in recorded) * 1e3
-               for k, n in enumerate(names)}
+    kern_fns = {"fwd_kernel": fwd, "bwd_partials_kernel": partials, "bwd_reduce_kernel": reduce}
+    n_launch = R * max(1, args.steps // R)
+    kern_us = {}
+    for name in names:
+        fn = kern_fns[name]
+        for i in range(R):
+            fn(sets[i])
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_launch):
+            fn(sets[i % R])
+        e1.record()
+        torch.cuda.synchronize()
+        kern_us[name] = e0.elapsed_time(e1) * 1e3 / n_launch
 
     step_bytes, per_kernel_bytes = algorithmic_bytes(B, K, SH2, D)
     flops = algorithmic_flops(B, K, SH2, D)

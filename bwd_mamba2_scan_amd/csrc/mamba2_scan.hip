@@ -55,7 +55,8 @@ constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
 constexpr int kBwdWaves = 8;
 constexpr int kBwdTargetGroups = 256;  // backward work-groups to aim for (one per CU)
 constexpr int kRedThreads = 256;
-constexpr int kRedElems = 64;      // output elements per reduce work-group
+constexpr int kRedQuads = 32;      // output float4s per reduce work-group
+constexpr int kRedGroups = kRedThreads / kRedQuads;  // slice groups per output
 
 __device__ __forceinline__ v4f mfma16x16x4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -73,6 +74,10 @@ __device__ __forceinline__ int plane_index(int smp, int n) { return (smp >> 2) *
 //   LDS   = 3 * SH2 * 16 * 4 B (weights) + 16 KiB (a|b exchange) + 8 KiB (c).
 // Work-group w runs on XCD w % 8; the NG state groups of one sample block are
 // given consecutive rounds on the same XCD so their h_history reads share L2.
+//
+// Every wave issues all of its history loads for the first round before the
+// weight slab is staged (loads complete in order, so the MFMAs then consume
+// them as they land), and the loads of round r+1 before the scan of round r.
 template <int NKC>  // SH2 / 16 trunk chunks
 __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     int B, int K, int NG, int NB,
@@ -80,6 +85,8 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
     float* __restrict__ ctx, float* __restrict__ saved) {
   constexpr int SH2 = NKC * 16;
+  constexpr int NE = (NKC * 64 + kFwdWaves * 64 - 1) / (kFwdWaves * 64);  // slab entries per thread
+  constexpr int NCR = (NKC + kFwdWaves - 1) / kFwdWaves;                   // readout chunks per wave
   __shared__ v4f sWa[NKC * 64];
   __shared__ v4f sWb[NKC * 64];
   __shared__ v4f sWc[NKC * 64];
@@ -100,42 +107,68 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   const int kg = lane >> 4;  // k-group of the A/B operands, row quad of the result
   const int m = lane & 15;   // row of A (sample) / column of B and result (state)
 
-  // Weight slab in B-operand layout: entry (kc, lane) holds
-  // W[kc*16 + 4*(lane>>4) + i][sg*16 + (lane&15)] for i = 0..3.
-  for (int e = tid; e < NKC * 64; e += kFwdWaves * 64) {
-    const int kc = e >> 6, l = e & 63;
-    const int j0 = kc * 16 + 4 * (l >> 4);
-    const int s = sg * kGroup + (l & 15);
-    v4f a, b, c;
+  // (1) weight slab entries of this thread.  Entry (kc, l) holds
+  // W[kc*16 + 4*(l>>4) + i][sg*16 + (l&15)] for i = 0..3.
+  v4f wra[NE], wrb[NE], wrc[NE];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = WA[(size_t)(j0 + i) * D + s];
-      b[i] = WB[(size_t)(j0 + i) * D + s];
-      c[i] = WC[(size_t)(j0 + i) * D + s];
+  for (int ie = 0; ie < NE; ++ie) {
+    const int e = tid + ie * kFwdWaves * 64;
+    if (e < NKC * 64) {
+      const int kc = e >> 6, l = e & 63;
+      const int j0 = kc * 16 + 4 * (l >> 4);
+      const int s = sg * kGroup + (l & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wra[ie][i] = WA[(size_t)(j0 + i) * D + s];
+        wrb[ie][i] = WB[(size_t)(j0 + i) * D + s];
+        wrc[ie][i] = WC[(size_t)(j0 + i) * D + s];
+      }
     }
-    sWa[e] = a;
-    sWb[e] = b;
-    sWc[e] = c;
+  }
+
+  // (2) A-operand row of this lane: sample blk*16 + m, clamped into range
+  // (rows of samples >= B are computed but never stored and never reach a
+  // gradient).  Readout chunks kc = wave + 8r, then this wave's first step.
+  const int smp_a = min(blk * kBlock + m, B - 1);
+  const float* crow = hs2 + (size_t)smp_a * SH2 + 4 * kg;
+  v4f hc[NCR];
+#pragma unroll
+  for (int r = 0; r < NCR; ++r) {
+    const int kc = wave + kFwdWaves * r;
+    if (kc < NKC) hc[r] = ld4(crow + kc * 16);
+  }
+  const float* hbase = H + (size_t)smp_a * K * SH2 + 4 * kg;
+  v4f hv[NKC];
+  if (wave < K) {
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) hv[kc] = ld4(hbase + (size_t)wave * SH2 + kc * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int ie = 0; ie < NE; ++ie) {
+    const int e = tid + ie * kFwdWaves * 64;
+    if (e < NKC * 64) {
+      sWa[e] = wra[ie];
+      sWb[e] = wrb[ie];
+      sWc[e] = wrc[ie];
+    }
   }
   __syncthreads();
 
-  // A-operand row of this lane: sample blk*16 + m, clamped into range (rows of
-  // samples >= B are computed but never stored and never reach a gradient).
-  const int smp_a = min(blk * kBlock + m, B - 1);
-
-  // Readout c: wave w takes trunk chunks kc = w, w+8, ...
+  // (3) readout partial over this wave's chunks
   {
-    const float* hrow = hs2 + (size_t)smp_a * SH2 + 4 * kg;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      if ((kc & (kFwdWaves - 1)) != wave) continue;
-      const v4f av = ld4(hrow + kc * 16);
-      const v4f bv = sWc[kc * 64 + lane];
-      acc = mfma16x16x4(av[0], bv[0], acc);
-      acc = mfma16x16x4(av[1], bv[1], acc);
-      acc = mfma16x16x4(av[2], bv[2], acc);
-      acc = mfma16x16x4(av[3], bv[3], acc);
+    for (int r = 0; r < NCR; ++r) {
+      const int kc = wave + kFwdWaves * r;
+      if (kc < NKC) {
+        const v4f bv = sWc[kc * 64 + lane];
+        acc = mfma16x16x4(hc[r][0], bv[0], acc);
+        acc = mfma16x16x4(hc[r][1], bv[1], acc);
+        acc = mfma16x16x4(hc[r][2], bv[2], acc);
+        acc = mfma16x16x4(hc[r][3], bv[3], acc);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) sC[wave][(4 * kg + r) * kGroup + m] = acc[r];
@@ -155,10 +188,6 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   for (int ch = 0; ch < nchunks; ++ch) {
     const int t = ch * kChunk + wave;
     if (t < K) {
-      const float* hrow = H + ((size_t)smp_a * K + t) * SH2 + 4 * kg;
-      v4f hv[NKC];
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) hv[kc] = ld4(hrow + kc * 16);
       v4f acca = {0.f, 0.f, 0.f, 0.f};
       v4f accb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -171,6 +200,12 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
           accb = mfma16x16x4(hv[kc][i], wb[i], accb);
         }
       }
+      // next round's loads go out before this round's exchange and scan
+      if (t + kChunk < K) {
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) hv[kc] = ld4(hbase + (size_t)(t + kChunk) * SH2 + kc * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         sXa[wave][(4 * kg + r) * kGroup + m] = acca[r];
@@ -260,6 +295,95 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
 //   N = states sg*16 + n, K = the 4 samples 4*kg + i of step i.
 //   A lane (kg, m): H[sample 4kg+i][t][jb*64 + 4m + q]
 //   B lane (kg, n): d_x[sample 4kg+i][t][n]
+//
+// Units: each sample block contributes K "step" units (H^T [d_a|d_b] at one
+// history step) and one "readout" unit (h_s2^T d_c).  Wave w takes units
+// w, w+8, ...; each wave keeps the loads of the next two units in flight
+// while it multiplies the current one.
+struct BwdUnit {
+  v4f h[4];   // A operands: 4 rows (samples 4kg+i) x 4 features
+  v4f al;     // alpha_t (step unit) or x_K (readout unit), samples 4kg..4kg+3
+  v4f be;     // beta_t (step unit)
+  float dc[4];  // d_context of samples 4kg+i, state n (unmasked)
+};
+
+struct BwdCtx {
+  int B, K, SH2, D, NG, sg, blk0, col, state, kg;
+  const float* H;
+  const float* hs2;
+  const float* saved;
+  const float* dctx;
+  size_t blk_stride;
+};
+
+__device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx& c, int lane) {
+  const int KU = c.K + 1;
+  const int bi = u / KU;
+  const int t = u - bi * KU;
+  const int blk = c.blk0 + bi;
+  const int sbase = blk * kBlock + 4 * c.kg;
+  const float* sv = c.saved + ((size_t)blk * c.NG + c.sg) * c.blk_stride;
+  if (t < c.K) {
+    U.al = ld4(sv + (size_t)(2 * t) * kPlane + 4 * lane);
+    U.be = ld4(sv + (size_t)(2 * t + 1) * kPlane + 4 * lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sc = min(sbase + i, c.B - 1);
+      U.h[i] = ld4(c.H + ((size_t)sc * c.K + t) * c.SH2 + c.col);
+      U.dc[i] = c.dctx[(size_t)sc * c.D + c.state];
+    }
+  } else {
+    U.al = ld4(sv + (size_t)(2 * c.K) * kPlane + 4 * lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sc = min(sbase + i, c.B - 1);
+      U.h[i] = ld4(c.hs2 + (size_t)sc * c.SH2 + c.col);
+      U.dc[i] = c.dctx[(size_t)sc * c.D + c.state];
+    }
+  }
+}
+
+__device__ __forceinline__ void bwd_compute(const BwdUnit& U, int u, const BwdCtx& c, v4f (&acc)[4][3],
+                                            float* __restrict__ d_a_out, float* __restrict__ d_b_out,
+                                            float* __restrict__ d_c_out, bool write_dbg) {
+  const int KU = c.K + 1;
+  const int bi = u / KU;
+  const int t = u - bi * KU;
+  const int sbase = (c.blk0 + bi) * kBlock + 4 * c.kg;
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  if (t < c.K) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = sbase + i;
+      const bool ok = s < c.B;
+      const float dc = ok ? U.dc[i] : 0.f;
+      const float da = dc * U.al[i];
+      const float db = dc * U.be[i];
+      const v4f h = ok ? U.h[i] : zero;
+      if (write_dbg && ok) {
+        if (d_a_out) d_a_out[((size_t)s * c.K + t) * c.D + c.state] = da;
+        if (d_b_out) d_b_out[((size_t)s * c.K + t) * c.D + c.state] = db;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q][0] = mfma16x16x4(h[q], da, acc[q][0]);
+        acc[q][1] = mfma16x16x4(h[q], db, acc[q][1]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = sbase + i;
+      const bool ok = s < c.B;
+      const float dcc = (ok ? U.dc[i] : 0.f) * U.al[i];
+      const v4f h = ok ? U.h[i] : zero;
+      if (write_dbg && ok && d_c_out) d_c_out[(size_t)s * c.D + c.state] = dcc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q][2] = mfma16x16x4(h[q], dcc, acc[q][2]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
     int B, int K, int SH2, int NG, int NB, int P, int BPW,
     const float* __restrict__ H, const float* __restrict__ hs2,
@@ -277,7 +401,6 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   if (p >= P) return;
   const int jb = v % NJB;
   const int sg = v / NJB;
-  const int D = NG * kGroup;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -286,11 +409,24 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   const int m = lane & 15;
   const bool write_dbg = (jb == 0);
 
-  const int blk0 = p * BPW;
-  const int nblk = min(NB - blk0, BPW);
-  const size_t blk_stride = (size_t)(2 * K + 1) * kPlane;
-  const int col = jb * kColBlock + 4 * m;
-  const int state = sg * kGroup + m;
+  BwdCtx c;
+  c.B = B;
+  c.K = K;
+  c.SH2 = SH2;
+  c.D = NG * kGroup;
+  c.NG = NG;
+  c.sg = sg;
+  c.blk0 = p * BPW;
+  c.col = jb * kColBlock + 4 * m;
+  c.state = sg * kGroup + m;
+  c.kg = kg;
+  c.H = H;
+  c.hs2 = hs2;
+  c.saved = saved;
+  c.dctx = dctx;
+  c.blk_stride = (size_t)(2 * K + 1) * kPlane;
+  const int nblk = min(NB - c.blk0, BPW);
+  const int n = nblk * (K + 1);
 
   v4f acc[4][3];
 #pragma unroll
@@ -298,64 +434,26 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
 #pragma unroll
     for (int pl = 0; pl < 3; ++pl) acc[q][pl] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int nunits = nblk * K;
-  for (int u = wave; u < nunits; u += kBwdWaves) {
-    const int blk = blk0 + u / K;
-    const int t = u - (u / K) * K;
-    const int sbase = blk * kBlock + 4 * kg;
-    const float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
-    const v4f al = ld4(sv + (size_t)(2 * t) * kPlane + 4 * lane);
-    const v4f be = ld4(sv + (size_t)(2 * t + 1) * kPlane + 4 * lane);
-    v4f hv[4];
-    float da[4], db[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = sbase + i;
-      const bool ok = s < B;
-      const int sc = ok ? s : B - 1;
-      const float dc = ok ? dctx[(size_t)sc * D + state] : 0.f;
-      da[i] = dc * al[i];
-      db[i] = dc * be[i];
-      const v4f h = ld4(H + ((size_t)sc * K + t) * SH2 + col);
-      hv[i] = ok ? h : v4f{0.f, 0.f, 0.f, 0.f};
-      if (write_dbg && ok) {
-        if (d_a_out) d_a_out[((size_t)s * K + t) * D + state] = da[i];
-        if (d_b_out) d_b_out[((size_t)s * K + t) * D + state] = db[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[q][0] = mfma16x16x4(hv[i][q], da[i], acc[q][0]);
-        acc[q][1] = mfma16x16x4(hv[i][q], db[i], acc[q][1]);
-      }
-    }
-  }
-
-  // dW_C: wave w takes the slice's sample blocks w, w+8, ...
-  for (int bi = wave; bi < nblk; bi += kBwdWaves) {
-    const int blk = blk0 + bi;
-    const int sbase = blk * kBlock + 4 * kg;
-    const float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
-    const v4f xk = ld4(sv + (size_t)(2 * K) * kPlane + 4 * lane);
-    v4f hv[4];
-    float dcc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = sbase + i;
-      const bool ok = s < B;
-      const int sc = ok ? s : B - 1;
-      const float dc = ok ? dctx[(size_t)sc * D + state] : 0.f;
-      dcc[i] = dc * xk[i];
-      const v4f h = ld4(hs2 + (size_t)sc * SH2 + col);
-      hv[i] = ok ? h : v4f{0.f, 0.f, 0.f, 0.f};
-      if (write_dbg && ok && d_c_out) d_c_out[(size_t)s * D + state] = dcc[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q][2] = mfma16x16x4(hv[i][q], dcc[i], acc[q][2]);
+  constexpr int S = kBwdWaves;
+  BwdUnit R0, R1, R2;
+  int u = wave;
+  if (u < n) bwd_load(R0, u, c, lane);
+  if (u + S < n) bwd_load(R1, u + S, c, lane);
+  while (u < n) {
+    if (u + 2 * S < n) bwd_load(R2, u + 2 * S, c, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    bwd_compute(R0, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    u += S;
+    if (u >= n) break;
+    if (u + 2 * S < n) bwd_load(R0, u + 2 * S, c, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    bwd_compute(R1, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    u += S;
+    if (u >= n) break;
+    if (u + 2 * S < n) bwd_load(R1, u + 2 * S, c, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    bwd_compute(R2, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    u += S;
   }
 
   // Result lane (g = kg, n = m), element r of tile q: feature row
@@ -381,45 +479,51 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
 
 // ---------------------------------------------------------------------------
 // Backward, phase 2: dW = sum over slices p = 0..P-1, in a fixed order.
-//   grid = ceil(NG * SH2 * 48 / 64), 256 threads: 64 elements x 4 quarters of
-//   the slice range; quarters are combined in order 0..3.
+//   grid = ceil(NG * SH2 * 48 / 4 / 32), 256 threads: 32 element quads x 8
+//   contiguous slice groups; the groups are combined in order 0..7.
 __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
     int SH2, int NG, int P, const float* __restrict__ ws,
     float* __restrict__ dWA, float* __restrict__ dWB, float* __restrict__ dWC) {
-  __shared__ float sPart[4][kRedElems];
+  __shared__ v4f sPart[kRedGroups][kRedQuads];
   const int per_sg = SH2 * 3 * kGroup;
-  const int total = NG * per_sg;
-  const int el = threadIdx.x & (kRedElems - 1);
-  const int qtr = threadIdx.x / kRedElems;
-  const int e = blockIdx.x * kRedElems + el;
-  const bool ok = e < total;
-  const int sg = ok ? e / per_sg : 0;
-  const int o = ok ? e - sg * per_sg : 0;
+  const int quads = NG * per_sg / 4;
+  const int ql = threadIdx.x % kRedQuads;
+  const int grp = threadIdx.x / kRedQuads;
+  const int qd = blockIdx.x * kRedQuads + ql;
+  const bool ok = qd < quads;
+  const int e = ok ? qd * 4 : 0;
+  const int sg = e / per_sg;
+  const int o = e - sg * per_sg;
 
-  const int pq = (P + 3) / 4;
-  const int p0 = qtr * pq;
-  const int p1 = min(P, p0 + pq);
-  float s = 0.f;
+  const int pc = (P + kRedGroups - 1) / kRedGroups;
+  const int p0 = grp * pc;
+  const int p1 = min(P, p0 + pc);
+  v4f s = {0.f, 0.f, 0.f, 0.f};
   if (ok) {
     const float* src = ws + (size_t)sg * P * per_sg + o;
-    for (int p = p0; p < p1; ++p) s += src[(size_t)p * per_sg];
+#pragma unroll 4
+    for (int pp = p0; pp < p1; ++pp) s += ld4(src + (size_t)pp * per_sg);
   }
-  sPart[qtr][el] = s;
+  sPart[grp][ql] = s;
   __syncthreads();
-  if (qtr != 0 || !ok) return;
-  const float tot = ((sPart[0][el] + sPart[1][el]) + sPart[2][el]) + sPart[3][el];
+  if (grp != 0 || !ok) return;
+  v4f tot = sPart[0][ql];
+#pragma unroll
+  for (int g = 1; g < kRedGroups; ++g) tot += sPart[g][ql];
 
   const int jb = o / (3 * kColBlock * kGroup);
   const int rem = o - jb * (3 * kColBlock * kGroup);
   const int pl = rem / (kColBlock * kGroup);
   const int rem2 = rem - pl * (kColBlock * kGroup);
   const int jl = rem2 / kGroup;
-  const int n = rem2 - jl * kGroup;
+  const int n = rem2 - jl * kGroup;  // multiple of 4
   const int D = NG * kGroup;
-  float* dst = pl == 0 ? dWA : (pl == 1 ? dWB : dWC);
-  dst[(size_t)(jb * kColBlock + jl) * D + sg * kGroup + n] = tot;
+  float* dst = (pl == 0 ? dWA : (pl == 1 ? dWB : dWC)) + (size_t)(jb * kColBlock + jl) * D + sg * kGroup + n;
+  dst[0] = tot[0];
+  dst[1] = tot[1];
+  dst[2] = tot[2];
+  dst[3] = tot[3];
 }
-
 // ---------------------------------------------------------------------------
 // Host side: shape checks and launch plans.
 struct Plan {
@@ -497,8 +601,8 @@ void launch_partials(const Plan& pl, const float* H, const float* hs2, const voi
 }
 
 void launch_reduce(const Plan& pl, const void* ws, float* dWA, float* dWB, float* dWC, hipStream_t st) {
-  const int total = pl.NG * pl.SH2 * 3 * kGroup;
-  const int grid = (total + kRedElems - 1) / kRedElems;
+  const int quads = pl.NG * pl.SH2 * 3 * kGroup / 4;
+  const int grid = (quads + kRedQuads - 1) / kRedQuads;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, st, pl.SH2, pl.NG, pl.P,
                      static_cast<const float*>(ws), dWA, dWB, dWC);
 }
