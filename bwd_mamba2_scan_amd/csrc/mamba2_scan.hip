@@ -75,9 +75,10 @@ __device__ __forceinline__ int plane_index(int smp, int n) { return (smp >> 2) *
 // Work-group w runs on XCD w % 8; the NG state groups of one sample block are
 // given consecutive rounds on the same XCD so their h_history reads share L2.
 //
-// Every wave issues all of its history loads for the first round before the
-// weight slab is staged (loads complete in order, so the MFMAs then consume
-// them as they land), and the loads of round r+1 before the scan of round r.
+// The weight slab is staged first; then every wave issues all of its history
+// loads for the first round at once (loads complete in order, so the MFMAs
+// consume them as they land), and the loads of round r+1 before the scan of
+// round r.
 template <int NKC>  // SH2 / 16 trunk chunks
 __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     int B, int K, int NG, int NB,
@@ -85,7 +86,6 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
     float* __restrict__ ctx, float* __restrict__ saved) {
   constexpr int SH2 = NKC * 16;
-  constexpr int NE = (NKC * 64 + kFwdWaves * 64 - 1) / (kFwdWaves * 64);  // slab entries per thread
   constexpr int NCR = (NKC + kFwdWaves - 1) / kFwdWaves;                   // readout chunks per wave
   __shared__ v4f sWa[NKC * 64];
   __shared__ v4f sWb[NKC * 64];
@@ -107,28 +107,43 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   const int kg = lane >> 4;  // k-group of the A/B operands, row quad of the result
   const int m = lane & 15;   // row of A (sample) / column of B and result (state)
 
-  // (1) weight slab entries of this thread.  Entry (kc, l) holds
+  // (1) Weight slab, staged before any history load is issued: the slab's
+  // loads would otherwise queue behind the CU's history stream and hold every
+  // MFMA back.  Each thread loads rows of W_X[j][sg*16 + 4*s4 .. +3] as float4
+  // and scatters them into the B-operand layout, where entry (kc, l) holds
   // W[kc*16 + 4*(l>>4) + i][sg*16 + (l&15)] for i = 0..3.
-  v4f wra[NE], wrb[NE], wrc[NE];
+  {
+    constexpr int NW4 = SH2 * 4;  // float4s per matrix slab
+    constexpr int NWT = (3 * NW4 + kFwdWaves * 64 - 1) / (kFwdWaves * 64);
+    v4f wr[NWT];
 #pragma unroll
-  for (int ie = 0; ie < NE; ++ie) {
-    const int e = tid + ie * kFwdWaves * 64;
-    if (e < NKC * 64) {
-      const int kc = e >> 6, l = e & 63;
-      const int j0 = kc * 16 + 4 * (l >> 4);
-      const int s = sg * kGroup + (l & 15);
+    for (int it = 0; it < NWT; ++it) {
+      const int f = tid + it * kFwdWaves * 64;
+      if (f < 3 * NW4) {
+        const int mat = f / NW4, r = f - mat * NW4;
+        const float* W = mat == 0 ? WA : (mat == 1 ? WB : WC);
+        wr[it] = ld4(W + (size_t)(r >> 2) * D + sg * kGroup + 4 * (r & 3));
+      }
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wra[ie][i] = WA[(size_t)(j0 + i) * D + s];
-        wrb[ie][i] = WB[(size_t)(j0 + i) * D + s];
-        wrc[ie][i] = WC[(size_t)(j0 + i) * D + s];
+    for (int it = 0; it < NWT; ++it) {
+      const int f = tid + it * kFwdWaves * 64;
+      if (f < 3 * NW4) {
+        const int mat = f / NW4, r = f - mat * NW4;
+        const int j = r >> 2, s4 = r & 3;
+        float* dst = reinterpret_cast<float*>(mat == 0 ? sWa : (mat == 1 ? sWb : sWc));
+        const int base = ((j >> 4) * 64 + 16 * ((j >> 2) & 3) + 4 * s4) * 4 + (j & 3);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[base + 4 * q] = wr[it][q];
       }
     }
   }
+  __syncthreads();
 
   // (2) A-operand row of this lane: sample blk*16 + m, clamped into range
   // (rows of samples >= B are computed but never stored and never reach a
-  // gradient).  Readout chunks kc = wave + 8r, then this wave's first step.
+  // gradient).  Readout chunks kc = wave + 8r, then this wave's first step:
+  // all issued now, consumed by the MFMAs below as they land.
   const int smp_a = min(blk * kBlock + m, B - 1);
   const float* crow = hs2 + (size_t)smp_a * SH2 + 4 * kg;
   v4f hc[NCR];
@@ -144,17 +159,6 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     for (int kc = 0; kc < NKC; ++kc) hv[kc] = ld4(hbase + (size_t)wave * SH2 + kc * 16);
   }
   __builtin_amdgcn_sched_barrier(0);
-
-#pragma unroll
-  for (int ie = 0; ie < NE; ++ie) {
-    const int e = tid + ie * kFwdWaves * 64;
-    if (e < NKC * 64) {
-      sWa[e] = wra[ie];
-      sWb[e] = wrb[ie];
-      sWc[e] = wrc[ie];
-    }
-  }
-  __syncthreads();
 
   // (3) readout partial over this wave's chunks
   {
@@ -228,8 +232,10 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
         if (tt < tn) {
           const float a = sXa[tt][idx];
           const float b = sXb[tt][idx];
-          const float e = expf(-a);
-          const float g = 1.f / (1.f + e);
+          // sigmoid(a) = 1 / (1 + e^-a) from the hardware exp2 and reciprocal
+          // (each within ~1 ulp); e = inf gives g = 0, never NaN.
+          const float e = __expf(-a);
+          const float g = __builtin_amdgcn_rcpf(1.f + e);
           // 1 - g, computed without cancellation: e*g = e/(1+e) for a > 0.
           const float omg = a > 0.f ? e * g : 1.f - g;
           U[tt] = x * g * omg;
@@ -629,8 +635,8 @@ int mamba2_scan_fwd(int B, int K, int SH2, int STATE_D, const float* h_history, 
   if (st != MAMBA2_SCAN_OK) return st;
   if (!h_history || !h_s2 || !W_A || !W_B || !W_C || !context || !saved) return MAMBA2_SCAN_ENULL;
   if (saved_bytes < pl.saved_bytes) return MAMBA2_SCAN_ESIZE;
-  if (!aligned16(h_history) || !aligned16(h_s2) || !aligned16(saved) || !aligned4(W_A) || !aligned4(W_B) ||
-      !aligned4(W_C) || !aligned4(context))
+  if (!aligned16(h_history) || !aligned16(h_s2) || !aligned16(saved) || !aligned16(W_A) || !aligned16(W_B) ||
+      !aligned16(W_C) || !aligned4(context))
     return MAMBA2_SCAN_EALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* sv = static_cast<float*>(saved);
@@ -700,7 +706,7 @@ const char* mamba2_scan_strerror(int status) {
     case MAMBA2_SCAN_EUNSUPPORTED: return "unsupported shape (STATE_D in {16,32,64}; SH2 % 64 == 0, SH2 <= 512)";
     case MAMBA2_SCAN_ENULL: return "a required pointer is NULL";
     case MAMBA2_SCAN_ESIZE: return "saved or workspace buffer is smaller than required";
-    case MAMBA2_SCAN_EALIGN: return "pointer misaligned (h_history, h_s2, saved, workspace need 16 bytes)";
+    case MAMBA2_SCAN_EALIGN: return "pointer misaligned (inputs, saved and workspace need 16 bytes)";
     case MAMBA2_SCAN_EHIP: return "HIP runtime error while enqueuing a kernel";
     default: return "unknown status";
   }

@@ -27,8 +27,8 @@
  *     work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *   - Supported shapes: B >= 1, K >= 1, STATE_D in {16, 32, 64},
  *     SH2 a multiple of 64 with 64 <= SH2 <= 512.
- *   - h_history, h_s2, saved and workspace must be 16-byte aligned; the other
- *     pointers 4-byte aligned.
+ *   - h_history, h_s2, W_A, W_B, W_C, saved and workspace must be 16-byte
+ *     aligned; the other pointers 4-byte aligned.
  *   - Every argument check runs before any work is enqueued.  On a nonzero
  *     return nothing has been written, except after MAMBA2_SCAN_EHIP.
  *   - Outputs are overwritten, never accumulated into.

@@ -83,8 +83,8 @@ def test_fwd_argument_checks(L):
         assert L.mamba2_scan_fwd(*_fwd_args(dims, ptrs, need)) == m2.ENULL, i
     # saved too small
     assert L.mamba2_scan_fwd(*_fwd_args(dims, [good] * 7, need - 4)) == m2.ESIZE
-    # misaligned: 16 bytes for h_history, h_s2, saved (slots 0, 1, 6); 4 for the rest
-    for i, off in ((0, 4), (1, 8), (6, 12), (2, 2), (5, 1)):
+    # misaligned: 16 bytes for h_history, h_s2, W_A/B/C, saved (slots 0-4, 6); 4 for context
+    for i, off in ((0, 4), (1, 8), (6, 12), (2, 2), (3, 4), (4, 8), (5, 1)):
         ptrs = [good] * 7
         ptrs[i] = ctypes.c_void_p(0x10000 + off)
         assert L.mamba2_scan_fwd(*_fwd_args(dims, ptrs, need)) == m2.EALIGN, i
