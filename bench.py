@@ -8,14 +8,15 @@ batch of seeded synthetic input already resident in HBM.  Prints one JSON line.
 Cold protocol (the headline): R input sets rotate so that no step's reads
 can be served from the 256 MB Infinity Cache.  Step s runs the forward of
 set s % R and the backward of set (s - R/2) % R, so between a set's forward
-and its backward R/2 other steps stream far more than the cache holds.  Each
-step is one captured HIP graph; the K timed steps are graph replays bracketed
-by device synchronisation.
+and its backward R/2 other steps stream far more than the cache holds.  A
+whole rotation of R steps is one captured HIP graph (single-step graphs cover
+a remainder); the K timed steps are graph replays bracketed by device
+synchronisation.
 
 Per-kernel durations come from HIP events (on the stream the kernels run on)
-around a batch of back-to-back launches of one kernel that walks the same
-rotation; the dominant kernel's algorithmic bytes over its mean duration give
-the roofline figure.
+around a captured batch of back-to-back launches of one kernel that walks the
+same rotation; the dominant kernel's algorithmic bytes over its mean duration
+give the roofline figure.
 """
 from __future__ import annotations
 
@@ -193,7 +194,7 @@ def main():
         fwd(s)
     torch.cuda.synchronize()
 
-    # ---- capture one graph per rotation phase
+    # ---- capture one graph per rotation phase, and one for a whole rotation
     stream = torch.cuda.Stream()
     graphs = []
     with torch.cuda.stream(stream):
@@ -205,14 +206,22 @@ def main():
             with torch.cuda.graph(g, stream=stream):
                 step(i)
             graphs.append(g)
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle, stream=stream):
+            for i in range(R):
+                step(i)
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        graphs[i % R].replay()
+    def run_steps(n):
+        for _ in range(n // R):
+            cycle.replay()
+        for i in range(n % R):
+            graphs[i].replay()
+
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % R].replay()
+    run_steps(args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -236,25 +245,32 @@ def main():
 
     # ---- per-kernel durations: HIP events around each kernel, cold rotation,
     # eager launches on the current stream (the one the kernels run on)
-    # Each kernel is timed over a batch of back-to-back launches that walk the
-    # rotation (so every launch reads a set the previous R-1 launches did not
-    # touch), bracketed by one event pair; the mean per launch is reported.
+    # Each kernel is timed over a captured batch of back-to-back launches that
+    # walks the rotation (so every launch reads a set the previous R-1 launches
+    # did not touch), bracketed by one event pair on the replay stream; the
+    # mean per launch is reported.
     names = ("fwd_kernel", "bwd_partials_kernel", "bwd_reduce_kernel")
     kern_fns = {"fwd_kernel": fwd, "bwd_partials_kernel": partials, "bwd_reduce_kernel": reduce}
-    n_launch = R * max(1, args.steps // R)
+    n_launch = R * max(2, args.steps // R)
     kern_us = {}
     for name in names:
         fn = kern_fns[name]
-        for i in range(R):
-            fn(sets[i])
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n_launch):
-            fn(sets[i % R])
-        e1.record()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n_launch):
+                    fn(sets[i % R])
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()  # warm-up replay
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
         torch.cuda.synchronize()
         kern_us[name] = e0.elapsed_time(e1) * 1e3 / n_launch
+        del g
 
     step_bytes, per_kernel_bytes = algorithmic_bytes(B, K, SH2, D)
     flops = algorithmic_flops(B, K, SH2, D)
@@ -279,7 +295,7 @@ def main():
         "config": {
             "workload": args.workload, "B": B, "K": K, "SH2": SH2, "STATE_D": D,
             "protocol": f"cold: {R} rotating input sets, fwd(set s) + bwd(set s-{R // 2}) per step, "
-                        "one HIP graph per step",
+                        f"HIP graph per {R}-step rotation",
         },
         "hbm_roofline_frac": round(roofline_us / (ms_per_step * 1e3), 4),
         "samples_per_s": round(B / (ms_per_step * 1e-3), 1),

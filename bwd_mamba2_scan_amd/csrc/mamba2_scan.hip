@@ -52,6 +52,7 @@ constexpr int kPlane = kBlock * kGroup;  // floats in one (sample, state) plane
 constexpr int kColBlock = 64;    // trunk features per backward column block
 constexpr int kFwdWaves = 8;
 constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
+constexpr int kFwdPrefetch = 6;    // history loads each forward wave keeps in flight
 constexpr int kBwdWaves = 8;
 constexpr int kBwdTargetGroups = 256;  // backward work-groups to aim for (one per CU)
 constexpr int kRedThreads = 256;
@@ -75,10 +76,12 @@ __device__ __forceinline__ int plane_index(int smp, int n) { return (smp >> 2) *
 // Work-group w runs on XCD w % 8; the NG state groups of one sample block are
 // given consecutive rounds on the same XCD so their h_history reads share L2.
 //
-// The weight slab is staged first; then every wave issues all of its history
-// loads for the first round at once (loads complete in order, so the MFMAs
-// consume them as they land), and the loads of round r+1 before the scan of
-// round r.
+// The weight slab is staged before any history load is issued (the vector
+// memory pipe returns data in issue order, so slab loads queued behind the
+// history stream would hold every MFMA back).  Each wave then keeps
+// min(kFwdPrefetch, SH2/16) history loads in flight: enough in total to
+// saturate HBM without queueing so deep that the first data arrives late.
+// The first loads of round r+1 go out before the scan of round r.
 template <int NKC>  // SH2 / 16 trunk chunks
 __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     int B, int K, int NG, int NB,
@@ -87,6 +90,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     float* __restrict__ ctx, float* __restrict__ saved) {
   constexpr int SH2 = NKC * 16;
   constexpr int NCR = (NKC + kFwdWaves - 1) / kFwdWaves;                   // readout chunks per wave
+  constexpr int PF = kFwdPrefetch < NKC ? kFwdPrefetch : NKC;              // history loads in flight
   __shared__ v4f sWa[NKC * 64];
   __shared__ v4f sWb[NKC * 64];
   __shared__ v4f sWc[NKC * 64];
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   v4f hv[NKC];
   if (wave < K) {
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) hv[kc] = ld4(hbase + (size_t)wave * SH2 + kc * 16);
+    for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4(hbase + (size_t)wave * SH2 + kc * 16);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -203,11 +207,14 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
           acca = mfma16x16x4(hv[kc][i], wa[i], acca);
           accb = mfma16x16x4(hv[kc][i], wb[i], accb);
         }
+        // keep PF loads of this step in flight
+        if (kc + PF < NKC) hv[kc + PF] = ld4(hbase + (size_t)t * SH2 + (kc + PF) * 16);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // next round's loads go out before this round's exchange and scan
+      // next round's first loads go out before this round's exchange and scan
       if (t + kChunk < K) {
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) hv[kc] = ld4(hbase + (size_t)(t + kChunk) * SH2 + kc * 16);
+        for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4(hbase + (size_t)(t + kChunk) * SH2 + kc * 16);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -304,8 +311,9 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
 //
 // Units: each sample block contributes K "step" units (H^T [d_a|d_b] at one
 // history step) and one "readout" unit (h_s2^T d_c).  Wave w takes units
-// w, w+8, ...; each wave keeps the loads of the next two units in flight
-// while it multiplies the current one.
+// w, w+8, ... (so the 8 waves of a work-group read neighbouring rows at the
+// same time); each wave keeps the loads of its next unit in flight while it
+// multiplies the current one.
 struct BwdUnit {
   v4f h[4];   // A operands: 4 rows (samples 4kg+i) x 4 features
   v4f al;     // alpha_t (step unit) or x_K (readout unit), samples 4kg..4kg+3
@@ -441,24 +449,18 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
     for (int pl = 0; pl < 3; ++pl) acc[q][pl] = v4f{0.f, 0.f, 0.f, 0.f};
 
   constexpr int S = kBwdWaves;
-  BwdUnit R0, R1, R2;
+  BwdUnit R0, R1;
   int u = wave;
   if (u < n) bwd_load(R0, u, c, lane);
-  if (u + S < n) bwd_load(R1, u + S, c, lane);
   while (u < n) {
-    if (u + 2 * S < n) bwd_load(R2, u + 2 * S, c, lane);
+    if (u + S < n) bwd_load(R1, u + S, c, lane);
     __builtin_amdgcn_sched_barrier(0);
     bwd_compute(R0, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
     u += S;
     if (u >= n) break;
-    if (u + 2 * S < n) bwd_load(R0, u + 2 * S, c, lane);
+    if (u + S < n) bwd_load(R0, u + S, c, lane);
     __builtin_amdgcn_sched_barrier(0);
     bwd_compute(R1, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
-    u += S;
-    if (u >= n) break;
-    if (u + 2 * S < n) bwd_load(R1, u + 2 * S, c, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    bwd_compute(R2, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
     u += S;
   }
 
@@ -560,7 +562,9 @@ int make_plan(int B, int K, int SH2, int D, Plan* pl) {
   pl->BPW = (pl->NB + p0 - 1) / p0;
   pl->P = (pl->NB + pl->BPW - 1) / pl->BPW;
   pl->saved_bytes = (size_t)pl->NB * pl->NG * (size_t)(2 * K + 1) * kPlane * sizeof(float);
-  pl->ws_bytes = (size_t)pl->NG * pl->P * (size_t)SH2 * 3 * kGroup * sizeof(float);
+  // Sized for p0 >= P slices: p0 never decreases as B grows, so neither does
+  // the workspace (P itself can, when BPW steps up).
+  pl->ws_bytes = (size_t)pl->NG * p0 * (size_t)SH2 * 3 * kGroup * sizeof(float);
   return MAMBA2_SCAN_OK;
 }
 

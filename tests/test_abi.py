@@ -41,11 +41,12 @@ def test_buffer_sizes():
         ws = m2.workspace_bytes(B, K, SH2, D)
         assert ws > 0 and ws % (SH2 * 48 * 4 * (D // 16)) == 0
     # workspace never shrinks as B grows
-    prev = 0
-    for B in list(range(1, 200, 7)) + [1024, 4096, 8192, 32768, 100000]:
-        ws = m2.workspace_bytes(B, 8, 256, 16)
-        assert ws >= prev
-        prev = ws
+    for K, SH2, D in ((8, 256, 16), (64, 256, 16), (8, 512, 64), (3, 192, 32)):
+        prev = 0
+        for B in list(range(1, 3000)) + [8192, 32768, 100000]:
+            ws = m2.workspace_bytes(B, K, SH2, D)
+            assert ws >= prev, (B, K, SH2, D)
+            prev = ws
     assert m2.workspace_bytes(8192, 8, 256, 16) == 64 * 256 * 48 * 4
 
 
