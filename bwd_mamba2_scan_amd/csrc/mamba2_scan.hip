@@ -65,6 +65,15 @@ __device__ __forceinline__ v4f mfma16x16x4(float a, float b, v4f c) {
 
 __device__ __forceinline__ v4f ld4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
 
+// Streaming accesses: data read once per kernel (h_history, h_s2) and results
+// no kernel reads back soon (context, saved terms, split-K slices) carry the
+// non-temporal hint, so they do not displace the lines that are reused (the
+// weight slab, the saved planes shared by the column blocks).
+__device__ __forceinline__ v4f ld4_stream(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+}
+__device__ __forceinline__ void st_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
 // Index of (sample smp in 0..15, state n in 0..15) inside a saved plane.  The
 // backward lane (quad kg, state n) reads samples 4kg..4kg+3 as one float4.
 __device__ __forceinline__ int plane_index(int smp, int n) { return (smp >> 2) * 64 + n * 4 + (smp & 3); }
@@ -154,13 +163,13 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
 #pragma unroll
   for (int r = 0; r < NCR; ++r) {
     const int kc = wave + kFwdWaves * r;
-    if (kc < NKC) hc[r] = ld4(crow + kc * 16);
+    if (kc < NKC) hc[r] = ld4_stream(crow + kc * 16);
   }
   const float* hbase = H + (size_t)smp_a * K * SH2 + 4 * kg;
   v4f hv[NKC];
   if (wave < K) {
 #pragma unroll
-    for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4(hbase + (size_t)wave * SH2 + kc * 16);
+    for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4_stream(hbase + (size_t)wave * SH2 + kc * 16);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -208,13 +217,13 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
           accb = mfma16x16x4(hv[kc][i], wb[i], accb);
         }
         // keep PF loads of this step in flight
-        if (kc + PF < NKC) hv[kc + PF] = ld4(hbase + (size_t)t * SH2 + (kc + PF) * 16);
+        if (kc + PF < NKC) hv[kc + PF] = ld4_stream(hbase + (size_t)t * SH2 + (kc + PF) * 16);
         __builtin_amdgcn_sched_barrier(0);
       }
       // next round's first loads go out before this round's exchange and scan
       if (t + kChunk < K) {
 #pragma unroll
-        for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4(hbase + (size_t)(t + kChunk) * SH2 + kc * 16);
+        for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4_stream(hbase + (size_t)(t + kChunk) * SH2 + kc * 16);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -267,8 +276,8 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   if (!scanner) return;
 
   const int b_glob = blk * kBlock + smp;
-  if (b_glob < B) ctx[(size_t)b_glob * D + sg * kGroup + m] = c * x;
-  sv[(size_t)(2 * K) * kPlane + pidx] = x;
+  if (b_glob < B) st_stream(&ctx[(size_t)b_glob * D + sg * kGroup + m], c * x);
+  st_stream(&sv[(size_t)(2 * K) * kPlane + pidx], x);
 
   // Reverse pass: P = c * prod_{v>t} g_v, beta_t = P, alpha_t = P * u_t.
   float P = c;
@@ -279,8 +288,8 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     for (int tt = kChunk - 1; tt >= 0; --tt) {
       if (tt < tn) {
         const int tg = ch * kChunk + tt;
-        sv[(size_t)(2 * tg) * kPlane + pidx] = P * U[tt];
-        sv[(size_t)(2 * tg + 1) * kPlane + pidx] = P;
+        st_stream(&sv[(size_t)(2 * tg) * kPlane + pidx], P * U[tt]);
+        st_stream(&sv[(size_t)(2 * tg + 1) * kPlane + pidx], P);
         P *= G[tt];
       }
     }
@@ -290,8 +299,8 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     float* pb = sv + (size_t)(2 * tg + 1) * kPlane + pidx;
     const float g = *pa;
     const float u = *pb;
-    *pa = P * u;
-    *pb = P;
+    st_stream(pa, P * u);
+    st_stream(pb, P);
     P *= g;
   }
 }
@@ -343,7 +352,7 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx& c, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int sc = min(sbase + i, c.B - 1);
-      U.h[i] = ld4(c.H + ((size_t)sc * c.K + t) * c.SH2 + c.col);
+      U.h[i] = ld4_stream(c.H + ((size_t)sc * c.K + t) * c.SH2 + c.col);
       U.dc[i] = c.dctx[(size_t)sc * c.D + c.state];
     }
   } else {
@@ -351,7 +360,7 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx& c, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int sc = min(sbase + i, c.B - 1);
-      U.h[i] = ld4(c.hs2 + (size_t)sc * c.SH2 + c.col);
+      U.h[i] = ld4_stream(c.hs2 + (size_t)sc * c.SH2 + c.col);
       U.dc[i] = c.dctx[(size_t)sc * c.D + c.state];
     }
   }
@@ -481,7 +490,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
     float s = sRed[0][e];
 #pragma unroll
     for (int w = 1; w < kBwdWaves; ++w) s += sRed[w][e];
-    out[e] = s;
+    st_stream(&out[e], s);
   }
 }
 
