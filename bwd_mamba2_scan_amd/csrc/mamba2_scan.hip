@@ -294,14 +294,40 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
       }
     }
   }
-  for (int tg = (nchunks - 1) * kChunk - 1; tg >= 0; --tg) {
-    float* pa = sv + (size_t)(2 * tg) * kPlane + pidx;
-    float* pb = sv + (size_t)(2 * tg + 1) * kPlane + pidx;
-    const float g = *pa;
-    const float u = *pb;
-    st_stream(pa, P * u);
-    st_stream(pb, P);
-    P *= g;
+  // Earlier rounds: their parked (g, u) are reloaded a whole round at a time,
+  // the next round's loads issued before this round's stores, so the pass
+  // costs about one load latency rather than one per step.
+  if (nchunks > 1) {
+    float gn[kChunk], un[kChunk];
+#pragma unroll
+    for (int tt = 0; tt < kChunk; ++tt) {
+      const int tg = (nchunks - 2) * kChunk + tt;
+      gn[tt] = sv[(size_t)(2 * tg) * kPlane + pidx];
+      un[tt] = sv[(size_t)(2 * tg + 1) * kPlane + pidx];
+    }
+    for (int ch = nchunks - 2; ch >= 0; --ch) {
+      float gc[kChunk], uc[kChunk];
+#pragma unroll
+      for (int tt = 0; tt < kChunk; ++tt) {
+        gc[tt] = gn[tt];
+        uc[tt] = un[tt];
+      }
+      if (ch > 0) {
+#pragma unroll
+        for (int tt = 0; tt < kChunk; ++tt) {
+          const int tg = (ch - 1) * kChunk + tt;
+          gn[tt] = sv[(size_t)(2 * tg) * kPlane + pidx];
+          un[tt] = sv[(size_t)(2 * tg + 1) * kPlane + pidx];
+        }
+      }
+#pragma unroll
+      for (int tt = kChunk - 1; tt >= 0; --tt) {
+        const int tg = ch * kChunk + tt;
+        st_stream(&sv[(size_t)(2 * tg) * kPlane + pidx], P * uc[tt]);
+        st_stream(&sv[(size_t)(2 * tg + 1) * kPlane + pidx], P);
+        P *= gc[tt];
+      }
+    }
   }
 }
 
