@@ -23,6 +23,10 @@
 //      d_c   = d_context * x_K,
 //    so the forward stores beta_t = c P_t, alpha_t = beta_t x_t g_t (1-g_t)
 //    and x_K ("saved"), and the backward only scales them by d_context.
+//    When K spans several 8-step rounds the forward stores each round's
+//    terms relative to the end of that round, plus one factor per round (the
+//    product of all later gates), which the backward multiplies in; so no
+//    pass over earlier rounds' terms is ever needed.
 //
 //  * bwd_partials_kernel: split-K tall reduction.  One work-group per
 //    (64-feature column block, state group, range of sample blocks); its 8
@@ -53,6 +57,7 @@ constexpr int kColBlock = 64;    // trunk features per backward column block
 constexpr int kFwdWaves = 8;
 constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
 constexpr int kFwdPrefetch = 6;    // history loads each forward wave keeps in flight
+constexpr int kRegRounds = 8;      // rounds whose gate product the forward keeps in registers
 constexpr int kBwdWaves = 8;
 constexpr int kBwdTargetGroups = 256;  // backward work-groups to aim for (one per CU)
 constexpr int kRedThreads = 256;
@@ -77,6 +82,13 @@ __device__ __forceinline__ void st_stream(float* p, float v) { __builtin_nontemp
 // Index of (sample smp in 0..15, state n in 0..15) inside a saved plane.  The
 // backward lane (quad kg, state n) reads samples 4kg..4kg+3 as one float4.
 __device__ __forceinline__ int plane_index(int smp, int n) { return (smp >> 2) * 64 + n * 4 + (smp & 3); }
+
+// Planes saved per (16-sample block, state group): alpha'_t, beta'_t for the
+// K steps, x_K, and one S_r per projection round when there is more than one.
+__host__ __device__ __forceinline__ int saved_planes(int K) {
+  const int rounds = (K + kChunk - 1) / kChunk;
+  return 2 * K + 1 + (rounds > 1 ? rounds : 0);
+}
 
 // ---------------------------------------------------------------------------
 // Forward.
@@ -196,12 +208,17 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   const bool scanner = wave < 4;
   const int smp = 4 * wave + kg;
   const int pidx = plane_index(smp & 15, m);
-  const size_t blk_stride = (size_t)(2 * K + 1) * kPlane;
+  // Saved planes of this (block, state group): alpha'_t and beta'_t for every
+  // step, x_K, then, when K spans several rounds, S_r for every round r.
+  const int nchunks = (K + kChunk - 1) / kChunk;
+  const size_t blk_stride = (size_t)saved_planes(K) * kPlane;
   float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
   float x = 0.f, c = 0.f;
   float G[kChunk], U[kChunk];
+  float Gr[kRegRounds];  // gate product of each round (rounds >= kRegRounds park theirs in saved)
+#pragma unroll
+  for (int i = 0; i < kRegRounds; ++i) Gr[i] = 1.f;
 
-  const int nchunks = (K + kChunk - 1) / kChunk;
   for (int ch = 0; ch < nchunks; ++ch) {
     const int t = ch * kChunk + wave;
     if (t < K) {
@@ -259,14 +276,28 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
           x = g * x + b;
         }
       }
-      if (ch + 1 < nchunks) {
-        // Park g_t and u_t in the alpha/beta slots; the reverse pass below
-        // reads them back (same thread) and overwrites them.
+      // Round-local reverse pass: beta'_t = c * prod of this round's later
+      // gates, alpha'_t = beta'_t * u_t.  The full terms are
+      // beta_t = S_r beta'_t and alpha_t = S_r alpha'_t with S_r the product
+      // of every gate of the later rounds; the backward applies S_r.
+      float P = c, gp = 1.f;
 #pragma unroll
-        for (int tt = 0; tt < kChunk; ++tt) {
+      for (int tt = kChunk - 1; tt >= 0; --tt) {
+        if (tt < tn) {
           const int tg = ch * kChunk + tt;
-          sv[(size_t)(2 * tg) * kPlane + pidx] = G[tt];
-          sv[(size_t)(2 * tg + 1) * kPlane + pidx] = U[tt];
+          st_stream(&sv[(size_t)(2 * tg) * kPlane + pidx], P * U[tt]);
+          st_stream(&sv[(size_t)(2 * tg + 1) * kPlane + pidx], P);
+          P *= G[tt];
+          gp *= G[tt];
+        }
+      }
+      if (nchunks > 1) {
+        if (ch < kRegRounds) {
+#pragma unroll
+          for (int i = 0; i < kRegRounds; ++i)
+            if (i == ch) Gr[i] = gp;
+        } else {
+          sv[(size_t)(2 * K + 1 + ch) * kPlane + pidx] = gp;  // read back below, same thread
         }
       }
     }
@@ -279,54 +310,21 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   if (b_glob < B) st_stream(&ctx[(size_t)b_glob * D + sg * kGroup + m], c * x);
   st_stream(&sv[(size_t)(2 * K) * kPlane + pidx], x);
 
-  // Reverse pass: P = c * prod_{v>t} g_v, beta_t = P, alpha_t = P * u_t.
-  float P = c;
-  {
-    const int ch = nchunks - 1;
-    const int tn = K - ch * kChunk;
-#pragma unroll
-    for (int tt = kChunk - 1; tt >= 0; --tt) {
-      if (tt < tn) {
-        const int tg = ch * kChunk + tt;
-        st_stream(&sv[(size_t)(2 * tg) * kPlane + pidx], P * U[tt]);
-        st_stream(&sv[(size_t)(2 * tg + 1) * kPlane + pidx], P);
-        P *= G[tt];
-      }
-    }
-  }
-  // Earlier rounds: their parked (g, u) are reloaded a whole round at a time,
-  // the next round's loads issued before this round's stores, so the pass
-  // costs about one load latency rather than one per step.
+  // S_r = product of the gates of rounds r+1 .. last (S_last = 1).
   if (nchunks > 1) {
-    float gn[kChunk], un[kChunk];
+    float S = 1.f;
+    for (int ch = nchunks - 1; ch >= 0; --ch) {
+      float* ps = &sv[(size_t)(2 * K + 1 + ch) * kPlane + pidx];
+      float g = 1.f;
+      if (ch < kRegRounds) {
 #pragma unroll
-    for (int tt = 0; tt < kChunk; ++tt) {
-      const int tg = (nchunks - 2) * kChunk + tt;
-      gn[tt] = sv[(size_t)(2 * tg) * kPlane + pidx];
-      un[tt] = sv[(size_t)(2 * tg + 1) * kPlane + pidx];
-    }
-    for (int ch = nchunks - 2; ch >= 0; --ch) {
-      float gc[kChunk], uc[kChunk];
-#pragma unroll
-      for (int tt = 0; tt < kChunk; ++tt) {
-        gc[tt] = gn[tt];
-        uc[tt] = un[tt];
+        for (int i = 0; i < kRegRounds; ++i)
+          if (i == ch) g = Gr[i];
+      } else {
+        g = *ps;
       }
-      if (ch > 0) {
-#pragma unroll
-        for (int tt = 0; tt < kChunk; ++tt) {
-          const int tg = (ch - 1) * kChunk + tt;
-          gn[tt] = sv[(size_t)(2 * tg) * kPlane + pidx];
-          un[tt] = sv[(size_t)(2 * tg + 1) * kPlane + pidx];
-        }
-      }
-#pragma unroll
-      for (int tt = kChunk - 1; tt >= 0; --tt) {
-        const int tg = ch * kChunk + tt;
-        st_stream(&sv[(size_t)(2 * tg) * kPlane + pidx], P * uc[tt]);
-        st_stream(&sv[(size_t)(2 * tg + 1) * kPlane + pidx], P);
-        P *= gc[tt];
-      }
+      st_stream(ps, S);
+      S *= g;
     }
   }
 }
@@ -351,8 +349,9 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
 // multiplies the current one.
 struct BwdUnit {
   v4f h[4];   // A operands: 4 rows (samples 4kg+i) x 4 features
-  v4f al;     // alpha_t (step unit) or x_K (readout unit), samples 4kg..4kg+3
-  v4f be;     // beta_t (step unit)
+  v4f al;     // alpha'_t (step unit) or x_K (readout unit), samples 4kg..4kg+3
+  v4f be;     // beta'_t (step unit)
+  v4f sr;     // S_r of the step's round (1 when K fits one round)
   float dc[4];  // d_context of samples 4kg+i, state n (unmasked)
 };
 
@@ -363,6 +362,7 @@ struct BwdCtx {
   const float* saved;
   const float* dctx;
   size_t blk_stride;
+  bool rounds;  // K spans more than one round: apply S_r
 };
 
 __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx& c, int lane) {
@@ -375,6 +375,7 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx& c, int
   if (t < c.K) {
     U.al = ld4(sv + (size_t)(2 * t) * kPlane + 4 * lane);
     U.be = ld4(sv + (size_t)(2 * t + 1) * kPlane + 4 * lane);
+    U.sr = c.rounds ? ld4(sv + (size_t)(2 * c.K + 1 + t / kChunk) * kPlane + 4 * lane) : v4f{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int sc = min(sbase + i, c.B - 1);
@@ -405,7 +406,7 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, int u, const BwdCt
     for (int i = 0; i < 4; ++i) {
       const int s = sbase + i;
       const bool ok = s < c.B;
-      const float dc = ok ? U.dc[i] : 0.f;
+      const float dc = ok ? U.dc[i] * U.sr[i] : 0.f;
       const float da = dc * U.al[i];
       const float db = dc * U.be[i];
       const v4f h = ok ? U.h[i] : zero;
@@ -473,7 +474,8 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   c.hs2 = hs2;
   c.saved = saved;
   c.dctx = dctx;
-  c.blk_stride = (size_t)(2 * K + 1) * kPlane;
+  c.blk_stride = (size_t)saved_planes(K) * kPlane;
+  c.rounds = K > kChunk;
   const int nblk = min(NB - c.blk0, BPW);
   const int n = nblk * (K + 1);
 
@@ -596,7 +598,7 @@ int make_plan(int B, int K, int SH2, int D, Plan* pl) {
   if (p0 > pl->NB) p0 = pl->NB;
   pl->BPW = (pl->NB + p0 - 1) / p0;
   pl->P = (pl->NB + pl->BPW - 1) / pl->BPW;
-  pl->saved_bytes = (size_t)pl->NB * pl->NG * (size_t)(2 * K + 1) * kPlane * sizeof(float);
+  pl->saved_bytes = (size_t)pl->NB * pl->NG * (size_t)saved_planes(K) * kPlane * sizeof(float);
   // Sized for p0 >= P slices: p0 never decreases as B grows, so neither does
   // the workspace (P itself can, when BPW steps up).
   pl->ws_bytes = (size_t)pl->NG * p0 * (size_t)SH2 * 3 * kGroup * sizeof(float);

@@ -34,10 +34,14 @@ def test_strerror_covers_codes():
 
 
 def test_buffer_sizes():
-    # saved: per 16-sample block and state group, 2K+1 planes of 16x16 floats
-    for B, K, SH2, D in ((64, 8, 256, 16), (8192, 8, 256, 16), (17, 3, 128, 32), (1, 1, 64, 64)):
+    # saved: per 16-sample block and state group, 2K+1 planes of 16x16 floats,
+    # plus one plane per 8-step round when K spans more than one round
+    for B, K, SH2, D in ((64, 8, 256, 16), (8192, 8, 256, 16), (17, 3, 128, 32), (1, 1, 64, 64),
+                         (100, 9, 256, 16), (8192, 64, 256, 16), (3, 100, 64, 32)):
         nb = (B + 15) // 16
-        assert m2.saved_bytes(B, K, SH2, D) == nb * (D // 16) * (2 * K + 1) * 256 * 4
+        rounds = (K + 7) // 8
+        planes = 2 * K + 1 + (rounds if rounds > 1 else 0)
+        assert m2.saved_bytes(B, K, SH2, D) == nb * (D // 16) * planes * 256 * 4
         ws = m2.workspace_bytes(B, K, SH2, D)
         assert ws > 0 and ws % (SH2 * 48 * 4 * (D // 16)) == 0
     # workspace never shrinks as B grows

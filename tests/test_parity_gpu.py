@@ -77,7 +77,7 @@ def check_against_oracle(inputs, debug=True):
 
 
 # Shapes chosen to cover: one sample, ragged batches (B % 16 != 0), K = 1,
-# K across the 8-step projection rounds (9, 17, 64), every SH2 multiple of 64
+# K across the 8-step projection rounds (9, 17, 64, 80, 100), every SH2 multiple of 64
 # from 64 to 512, all three state widths, and partial slices in the backward.
 EDGE_SHAPES = [
     (1, 1, 64, 16),
@@ -93,6 +93,8 @@ EDGE_SHAPES = [
     (250, 5, 64, 64),
     (129, 1, 512, 32),
     (300, 12, 256, 16),
+    (20, 80, 64, 16),     # ten 8-step rounds: two beyond those held in registers
+    (5, 100, 128, 32),
 ]
 
 
