@@ -170,6 +170,30 @@ def backward(fwd: Forward, h_history, h_s2, d_context) -> Backward:
     return Backward(d_a=d_a, d_b=d_b, d_c=d_c, dW_A=dW_A, dW_B=dW_B, dW_C=dW_C)
 
 
+@dataclass
+class InputGrads:
+    d_h_history: np.ndarray  # [B, K, SH2]
+    d_h_s2: np.ndarray       # [B, SH2]
+
+
+def input_grads(bwd: Backward, W_A, W_B, W_C) -> InputGrads:
+    """Gradients of L with respect to the trunk inputs.
+
+    The pages stop at the weight gradients (plan Task 2 ends with the
+    weight-gradient GEMMs); training the trunk through the scan also needs
+    dL/dh_history and dL/dh_s2.  By the chain rule through the three
+    projections of plan Task 1 step 2:
+      d_h_history[b, t, :] = d_a[b, t, :] @ W_A^T + d_b[b, t, :] @ W_B^T
+      d_h_s2[b, :]         = d_c[b, :] @ W_C^T
+    """
+    B, K, D = bwd.d_a.shape
+    d_a = bwd.d_a.reshape(B * K, D)
+    d_b = bwd.d_b.reshape(B * K, D)
+    dH = d_a @ _f64(W_A).T + d_b @ _f64(W_B).T
+    dhs2 = bwd.d_c @ _f64(W_C).T
+    return InputGrads(d_h_history=dH.reshape(B, K, -1), d_h_s2=dhs2)
+
+
 def fwd_bwd(inputs: dict):
     """One forward + backward step on a dict from the seeded input generator."""
     f = forward(inputs["h_history"], inputs["h_s2"], inputs["W_A"], inputs["W_B"], inputs["W_C"])

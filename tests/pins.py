@@ -272,6 +272,28 @@ def check_invariants(orc):
     np.testing.assert_allclose(fc.context, -2.0 * f.context, rtol=1e-12, atol=1e-13)
 
 
+def check_input_grads_finite_difference(orc):
+    """Central differences of L with respect to every entry of h_history and h_s2.
+
+    Shapes (B, K, SH2, D) = (2, 3, 4, 2) and (1, 1, 3, 3); h = 1e-6.  Only
+    the oracle's forward enters the differences.
+    """
+    rng = np.random.default_rng(1010)
+    for B, K, SH2, D in ((2, 3, 4, 2), (1, 1, 3, 3)):
+        H, h_s2, W_A, W_B, W_C, d_ctx = _real_inputs(rng, B, K, SH2, D, wa_scale=1.0)
+        f = orc.forward(H, h_s2, W_A, W_B, W_C)
+        g = orc.input_grads(orc.backward(f, H, h_s2, d_ctx), W_A, W_B, W_C)
+
+        def L():
+            ff = orc.forward(H, h_s2, W_A, W_B, W_C)
+            return float(np.sum(d_ctx * ff.context))
+
+        for X, an in ((H, g.d_h_history), (h_s2, g.d_h_s2)):
+            fd = _fd_grad(L, X, 1e-6)
+            err = float(np.max(np.abs(fd - an)))
+            assert err <= 2e-8 * max(1.0, float(np.max(np.abs(an)))), ((B, K, SH2, D), err)
+
+
 ALL_PINS = [
     check_k1_closed_form,
     check_half_gate_geometric,
@@ -282,4 +304,5 @@ ALL_PINS = [
     check_reverse_scan_products,
     check_k1_no_gate_gradient,
     check_invariants,
+    check_input_grads_finite_difference,
 ]

@@ -77,8 +77,20 @@ def _forward_sum_readout(h_history, h_s2, W_A, W_B, W_C):
     return f
 
 
+def _input_grads_wrong_weight(bwd, W_A, W_B, W_C):
+    g = _ORIG_INPUT_GRADS(bwd, W_A, W_B, W_C)
+    B, K, D = bwd.d_a.shape
+    if g.d_h_history.shape[2] == D:  # only well-defined for square weights
+        return g
+    # plausible mistake: d_b multiplied by W_A instead of W_B
+    dH = bwd.d_a.reshape(B * K, D) @ _f64(W_A).T + bwd.d_b.reshape(B * K, D) @ _f64(W_A).T
+    g.d_h_history = dH.reshape(B, K, -1)
+    return g
+
+
 _ORIG_BACKWARD = orc.backward
 _ORIG_FORWARD = orc.forward
+_ORIG_INPUT_GRADS = orc.input_grads
 
 MUTANTS = {
     "gate_sign_flipped": ("logistic", lambda a: 1.0 / (1.0 + np.exp(_f64(a)))),
@@ -93,6 +105,7 @@ MUTANTS = {
     "dWC_from_d_context": ("backward", _backward_dwc_from_dcontext),
     "dWA_dWB_swapped": ("backward", _backward_swapped_planes),
     "readout_added_not_multiplied": ("forward", _forward_sum_readout),
+    "input_grad_uses_wrong_weight": ("input_grads", _input_grads_wrong_weight),
 }
 
 
