@@ -55,6 +55,8 @@ def algorithmic_bytes(B, K, SH2, D):
         "fwd_kernel": fwd,
         "bwd_partials_kernel": H + hs2 + vec,
         "bwd_reduce_kernel": W,
+        # optional input gradients: read W and d_context, write d_h_history and d_h_s2
+        "dinput_kernel": W + vec + H + hs2,
     }
     return fwd + bwd, per_kernel
 
@@ -129,10 +131,19 @@ def parity_gate(m2, torch, t, inputs):
         rel = float(np.sum(np.abs(g[k].cpu().numpy() - ref)) / np.sum(np.abs(ref)))
         worst_l1 = max(worst_l1, rel)
         ok = ok and rel <= 1e-3
+    dH, dhs2 = m2.bwd_input(t["W_A"], t["W_B"], t["W_C"], saved, t["d_context"], inputs["h_history"].shape[1])
+    torch.cuda.synchronize()
+    ig = orc.input_grads(b, inputs["W_A"], inputs["W_B"], inputs["W_C"])
+    in_err = 0.0
+    for got, ref in ((dH, ig.d_h_history), (dhs2, ig.d_h_s2)):
+        v = got.cpu().numpy().astype(np.float64)
+        in_err = max(in_err, float(np.max(np.abs(v - ref) / (1 + np.abs(ref)))))
+    ok = ok and in_err <= 1e-4
     if not ok:
-        raise SystemExit(f"parity gate failed on the benchmarked workload (worst dW L1 {worst_l1:.3e})")
+        raise SystemExit(f"parity gate failed on the benchmarked workload (worst dW L1 {worst_l1:.3e}, "
+                         f"worst input-gradient error {in_err:.3e})")
     return {"context_max_abs_err": float(np.max(np.abs(c - f.context))), "dW_worst_L1_rel": worst_l1,
-            "mean_gate": float(np.mean(f.g))}
+            "input_grads_max_rel_err": in_err, "mean_gate": float(np.mean(f.g))}
 
 
 def main():
@@ -175,6 +186,8 @@ def main():
         s["saved"] = m2.alloc_saved(B, K, SH2, D, dev)
         s["ws"] = m2.alloc_workspace(B, K, SH2, D, dev)
         s["dW"] = [torch.empty((SH2, D), device=dev) for _ in range(3)]
+        s["dH"] = torch.empty((B, K, SH2), device=dev)
+        s["dhs2"] = torch.empty((B, SH2), device=dev)
         sets.append(s)
     del base
 
@@ -186,6 +199,10 @@ def main():
 
     def reduce(s):
         m2.bwd_reduce(B, K, SH2, D, s["ws"], *s["dW"])
+
+    def dinput(s):
+        m2.bwd_input(s["W_A"], s["W_B"], s["W_C"], s["saved"], s["d_context"], K, d_h_history=s["dH"],
+                     d_h_s2=s["dhs2"])
 
     def step(i):
         fwd(sets[i % R])
@@ -254,10 +271,11 @@ def main():
     # did not touch), bracketed by one event pair on the replay stream; the
     # mean per launch is reported.
     names = ("fwd_kernel", "bwd_partials_kernel", "bwd_reduce_kernel")
-    kern_fns = {"fwd_kernel": fwd, "bwd_partials_kernel": partials, "bwd_reduce_kernel": reduce}
+    kern_fns = {"fwd_kernel": fwd, "bwd_partials_kernel": partials, "bwd_reduce_kernel": reduce,
+                "dinput_kernel": dinput}
     n_launch = R * max(2, args.steps // R)
     kern_us = {}
-    for name in names:
+    for name in names + ("dinput_kernel",):
         fn = kern_fns[name]
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
@@ -319,8 +337,14 @@ def main():
         "algorithmic_flops_per_step": flops,
         "achieved_GBps_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "warm_ms_per_step": round(warm_ms, 5),
-        "kernel_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "kernel_us": {n: round(kern_us[n], 2) for n in names},
         "roofline": roof,
+        # not part of the step: the optional input gradients, timed the same way
+        "input_grads": {"kernel": "dinput_kernel", "us": round(kern_us["dinput_kernel"], 2), "bound": "hbm",
+                        "achieved": round(per_kernel_bytes["dinput_kernel"] / (kern_us["dinput_kernel"] * 1e-6) / 1e9, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(per_kernel_bytes["dinput_kernel"] / (kern_us["dinput_kernel"] * 1e-6) / 1e9
+                                      / HBM_PEAK_GBS, 4)},
         "parity": gate,
     }
     if not args.no_cpu_baseline:

@@ -8,6 +8,7 @@ The entry points mirror include/mamba2_scan.h:
     fwd(h_history, h_s2, W_A, W_B, W_C)         -> (context, saved)
     bwd(h_history, h_s2, saved, d_context)      -> dict(dW_A, dW_B, dW_C[, d_a, d_b, d_c])
     bwd_partials(...), bwd_reduce(...)          -- the two phases of bwd
+    bwd_input(W_A, W_B, W_C, saved, d_context, K) -> (d_h_history, d_h_s2)
     saved_bytes(B, K, SH2, D), workspace_bytes(B, K, SH2, D)
 """
 from __future__ import annotations
@@ -48,6 +49,7 @@ _SIGNATURES = {
     "mamba2_scan_bwd": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 8 + [_c_size, _c_vp]),
     "mamba2_scan_bwd_partials": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 5 + [_c_size, _c_vp]),
     "mamba2_scan_bwd_reduce": (_c_int, [_c_int] * 4 + [_c_vp, _c_size] + [_c_vp] * 4),
+    "mamba2_scan_bwd_input": (_c_int, [_c_int] * 4 + [_c_vp] * 4 + [_c_size] + [_c_vp] * 4),
     "mamba2_scan_strerror": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -236,3 +238,34 @@ def bwd_reduce(B, K, SH2, D, workspace, dW_A, dW_B, dW_C, *, stream=None):
     st = lib().mamba2_scan_bwd_reduce(B, K, SH2, D, _ptr(workspace), workspace.numel() * 4, _ptr(dW_A),
                                       _ptr(dW_B), _ptr(dW_C), _stream(stream, dev))
     _raise(st, "mamba2_scan_bwd_reduce")
+
+
+def bwd_input(W_A, W_B, W_C, saved, d_context, K, *, d_h_history=None, d_h_s2=None, want=("h_history", "h_s2"),
+              stream=None):
+    """Input gradients (d_h_history [B, K, SH2], d_h_s2 [B, SH2]) from the forward's saved terms.
+
+    `want` names the outputs to compute; an output not wanted comes back as None.
+    """
+    torch = _torch()
+    if W_A.dim() != 2 or d_context.dim() != 2:
+        raise ValueError("W_A must be [SH2, D] and d_context [B, D]")
+    SH2, D = (int(v) for v in W_A.shape)
+    B = int(d_context.shape[0])
+    K = int(K)
+    dev = W_A.device
+    for name, w in (("W_A", W_A), ("W_B", W_B), ("W_C", W_C)):
+        _check(w, name, (SH2, D), dev)
+    _check(saved, "saved", None, dev)
+    _check(d_context, "d_context", (B, D), dev)
+    if "h_history" in want and d_h_history is None:
+        d_h_history = torch.empty((B, K, SH2), dtype=torch.float32, device=dev)
+    if "h_s2" in want and d_h_s2 is None:
+        d_h_s2 = torch.empty((B, SH2), dtype=torch.float32, device=dev)
+    if d_h_history is not None:
+        _check(d_h_history, "d_h_history", (B, K, SH2), dev)
+    if d_h_s2 is not None:
+        _check(d_h_s2, "d_h_s2", (B, SH2), dev)
+    st = lib().mamba2_scan_bwd_input(B, K, SH2, D, _ptr(W_A), _ptr(W_B), _ptr(W_C), _ptr(saved), saved.numel() * 4,
+                                     _ptr(d_context), _ptr(d_h_history), _ptr(d_h_s2), _stream(stream, dev))
+    _raise(st, "mamba2_scan_bwd_input")
+    return d_h_history, d_h_s2

@@ -78,6 +78,9 @@ __device__ __forceinline__ v4f ld4_stream(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
 }
 __device__ __forceinline__ void st_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st4_stream(float* p, v4f v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
+}
 
 // Index of (sample smp in 0..15, state n in 0..15) inside a saved plane.  The
 // backward lane (quad kg, state n) reads samples 4kg..4kg+3 as one float4.
@@ -570,6 +573,110 @@ __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
   dst[3] = tot[3];
 }
 // ---------------------------------------------------------------------------
+// Input gradients, an optional step past the pages' path (their backward
+// ends with the weight gradients).  By the chain rule through the three
+// projections:
+//   d_h_history[b][t][j] = sum_s d_a[b,t,s] W_A[j][s] + d_b[b,t,s] W_B[j][s]
+//   d_h_s2[b][j]         = sum_s d_c[b,s]   W_C[j][s]
+// with d_a, d_b, d_c formed from `saved` and d_context exactly as in the
+// backward.  Neither h_history nor h_s2 is read.
+//   grid = 8 * (SH2/64) * ceil(NB / 8), 512 threads.  Work-group: (16-sample
+//   block, 64-feature column block), the column blocks of one sample block on
+//   one XCD so they share the saved planes in L2.  Waves take units u = 0..K
+//   (history step u, or the readout when u = K) round-robin.
+// MFMA roles: M = 16 features (4 tiles), N = the 16 samples, K = the 2*D
+// (or D) states.  A lane (kg, m): W[feature m][state 4q+kg] from the
+// work-group's LDS copy of the column block's weights; B lane (kg, n):
+// d[sample n][state 4q+kg] from a per-wave LDS tile.  A result lane then
+// holds 4 consecutive features of one sample: one 16-byte store.
+template <int NGT>
+__global__ __launch_bounds__(kFwdWaves * 64) void dinput_kernel(
+    int B, int K, int SH2, int NB,
+    const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
+    const float* __restrict__ saved, const float* __restrict__ dctx,
+    float* __restrict__ dH, float* __restrict__ dhs2) {
+  constexpr int D = NGT * kGroup;
+  constexpr int DP = D + 1;  // padded rows: fewer LDS bank conflicts
+  __shared__ float sW[3][kColBlock][DP];
+  __shared__ float sDc[kBlock][DP];
+  __shared__ float sXk[kBlock][DP];
+  __shared__ float sA[kFwdWaves][kBlock][2 * D + 1];
+
+  const int NJB = SH2 / kColBlock;
+  const int xcd = blockIdx.x & 7;
+  const int round = blockIdx.x >> 3;
+  const int jb = round % NJB;
+  const int blk = (round / NJB) * 8 + xcd;
+  if (blk >= NB) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int kg = lane >> 4;
+  const int m = lane & 15;
+  const bool rounds = K > kChunk;
+  const size_t blk_stride = (size_t)saved_planes(K) * kPlane;
+
+  for (int e = tid; e < 3 * kColBlock * D; e += kFwdWaves * 64) {
+    const int mat = e / (kColBlock * D), r = e - mat * (kColBlock * D);
+    const int jl = r / D, st = r - jl * D;
+    const float* W = mat == 0 ? WA : (mat == 1 ? WB : WC);
+    sW[mat][jl][st] = W[(size_t)(jb * kColBlock + jl) * D + st];
+  }
+  for (int e = tid; e < kBlock * D; e += kFwdWaves * 64) {
+    const int sl = e / D, st = e - sl * D;
+    const int b = blk * kBlock + sl;
+    sDc[sl][st] = b < B ? dctx[(size_t)b * D + st] : 0.f;
+    sXk[sl][st] = saved[((size_t)blk * NGT + st / kGroup) * blk_stride + (size_t)(2 * K) * kPlane +
+                        plane_index(sl, st % kGroup)];
+  }
+  __syncthreads();
+
+  for (int u = wave; u <= K; u += kFwdWaves) {
+    const bool readout = (u == K);
+    if (readout ? dhs2 == nullptr : dH == nullptr) continue;
+    // this wave's A tile: d_a | d_b (or d_c) of the block's 16 samples
+    for (int e = lane; e < kBlock * D; e += 64) {
+      const int sl = e / D, st = e - sl * D;
+      if (readout) {
+        sA[wave][sl][st] = sDc[sl][st] * sXk[sl][st];
+      } else {
+        const float* sv = saved + ((size_t)blk * NGT + st / kGroup) * blk_stride;
+        const int pi = plane_index(sl, st % kGroup);
+        float dc = sDc[sl][st];
+        if (rounds) dc *= sv[(size_t)(2 * K + 1 + u / kChunk) * kPlane + pi];
+        sA[wave][sl][st] = dc * sv[(size_t)(2 * u) * kPlane + pi];
+        sA[wave][sl][D + st] = dc * sv[(size_t)(2 * u + 1) * kPlane + pi];
+      }
+    }
+    // The tile is written and read by this wave only, and a wave's LDS
+    // operations complete in order; keep the compiler from moving reads up.
+    __builtin_amdgcn_wave_barrier();
+    v4f acc[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) acc[jt] = v4f{0.f, 0.f, 0.f, 0.f};
+    const int steps = readout ? D / 4 : 2 * D / 4;
+    for (int q = 0; q < steps; ++q) {
+      const int k = 4 * q + kg;
+      const float d = sA[wave][m][k];
+      const int mat = readout ? 2 : (4 * q < D ? 0 : 1);
+      const int st = (readout || 4 * q < D) ? k : k - D;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) acc[jt] = mfma16x16x4(sW[mat][jt * 16 + m][st], d, acc[jt]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // result lane (g, n), element r: feature jb*64 + jt*16 + 4g + r, sample n
+    const int b = blk * kBlock + m;
+    if (b < B) {
+      float* dst = readout ? dhs2 + (size_t)b * SH2 : dH + ((size_t)b * K + u) * SH2;
+      dst += jb * kColBlock + 4 * kg;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) st4_stream(dst + jt * 16, acc[jt]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side: shape checks and launch plans.
 struct Plan {
   int B, K, SH2, D, NG, NB, NJB, V;
@@ -652,6 +759,14 @@ void launch_reduce(const Plan& pl, const void* ws, float* dWA, float* dWB, float
   const int grid = (quads + kRedQuads - 1) / kRedQuads;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, st, pl.SH2, pl.NG, pl.P,
                      static_cast<const float*>(ws), dWA, dWB, dWC);
+}
+
+template <int NGT>
+void launch_dinput(const Plan& pl, const float* WA, const float* WB, const float* WC, const float* sv,
+                   const float* dctx, float* dH, float* dhs2, hipStream_t st) {
+  const int grid = 8 * pl.NJB * ((pl.NB + 7) / 8);
+  hipLaunchKernelGGL(dinput_kernel<NGT>, dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NB, WA,
+                     WB, WC, sv, dctx, dH, dhs2);
 }
 
 }  // namespace
@@ -737,6 +852,28 @@ int mamba2_scan_bwd(int B, int K, int SH2, int STATE_D, const float* h_history, 
   st = launch_status();
   if (st != MAMBA2_SCAN_OK) return st;
   launch_reduce(pl, workspace, dW_A, dW_B, dW_C, s);
+  return launch_status();
+}
+
+int mamba2_scan_bwd_input(int B, int K, int SH2, int STATE_D, const float* W_A, const float* W_B,
+                          const float* W_C, const void* saved, size_t saved_bytes, const float* d_context,
+                          float* d_h_history, float* d_h_s2, void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  if (!W_A || !W_B || !W_C || !saved || !d_context || (!d_h_history && !d_h_s2)) return MAMBA2_SCAN_ENULL;
+  if (saved_bytes < pl.saved_bytes) return MAMBA2_SCAN_ESIZE;
+  if (!aligned16(saved) || !aligned4(W_A) || !aligned4(W_B) || !aligned4(W_C) || !aligned4(d_context) ||
+      !aligned16(d_h_history) || !aligned16(d_h_s2))
+    return MAMBA2_SCAN_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* sv = static_cast<const float*>(saved);
+  switch (pl.NG) {
+    case 1: launch_dinput<1>(pl, W_A, W_B, W_C, sv, d_context, d_h_history, d_h_s2, s); break;
+    case 2: launch_dinput<2>(pl, W_A, W_B, W_C, sv, d_context, d_h_history, d_h_s2, s); break;
+    case 4: launch_dinput<4>(pl, W_A, W_B, W_C, sv, d_context, d_h_history, d_h_s2, s); break;
+    default: return MAMBA2_SCAN_EUNSUPPORTED;
+  }
   return launch_status();
 }
 

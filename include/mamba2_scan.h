@@ -126,6 +126,31 @@ int mamba2_scan_bwd_reduce(int B, int K, int SH2, int STATE_D,
                            float* dW_A, float* dW_B, float* dW_C,
                            void* stream);
 
+/*
+ * Input gradients, one step past the pages' backward (the implementation
+ * plan's Task 2 ends at the weight gradients; its Task 1 step 2 defines the
+ * projections these differentiate):
+ *   d_h_history[b][t][j] = sum_s d_a[b][t][s] W_A[j][s] + d_b[b][t][s] W_B[j][s]
+ *   d_h_s2[b][j]         = sum_s d_c[b][s] W_C[j][s]
+ * with d_a, d_b, d_c the same terms mamba2_scan_bwd forms from `saved` and
+ * d_context.  Reads W_A, W_B, W_C [SH2][STATE_D], `saved` (filled by
+ * mamba2_scan_fwd with the same B, K, SH2, STATE_D) and d_context
+ * [B][STATE_D]; never reads h_history or h_s2.  Overwrites
+ * d_h_history [B][K][SH2] and d_h_s2 [B][SH2] (row-major, caller-owned
+ * device memory, 16-byte aligned); either may be NULL to skip it, not both.
+ * Independent of mamba2_scan_bwd: the two may run in either order or on
+ * different streams once the forward has finished.
+ * Returns MAMBA2_SCAN_ENULL for a NULL input or both outputs NULL,
+ * MAMBA2_SCAN_ESIZE if saved_bytes is short, MAMBA2_SCAN_EALIGN for a
+ * misaligned pointer (saved, d_h_history, d_h_s2: 16 bytes; the rest: 4).
+ */
+int mamba2_scan_bwd_input(int B, int K, int SH2, int STATE_D,
+                          const float* W_A, const float* W_B, const float* W_C,
+                          const void* saved, size_t saved_bytes,
+                          const float* d_context,
+                          float* d_h_history, float* d_h_s2,
+                          void* stream);
+
 /* Static text for a status code. */
 const char* mamba2_scan_strerror(int status);
 

@@ -21,7 +21,8 @@ def test_exports_every_header_symbol(L):
     names = m2.header_functions()
     assert set(names) == {
         "mamba2_scan_saved_bytes", "mamba2_scan_bwd_workspace_bytes", "mamba2_scan_fwd",
-        "mamba2_scan_bwd", "mamba2_scan_bwd_partials", "mamba2_scan_bwd_reduce", "mamba2_scan_strerror",
+        "mamba2_scan_bwd", "mamba2_scan_bwd_partials", "mamba2_scan_bwd_reduce", "mamba2_scan_bwd_input",
+        "mamba2_scan_strerror",
     }
     for n in names:
         assert hasattr(L, n), n
@@ -71,6 +72,7 @@ def test_bad_dims(L, dims, code):
     assert L.mamba2_scan_bwd_partials(*dims, fake, fake, fake, 1 << 40, fake, None, None, None,
                                       fake, 1 << 40, None) == code
     assert L.mamba2_scan_bwd_reduce(*dims, fake, 1 << 40, fake, fake, fake, None) == code
+    assert L.mamba2_scan_bwd_input(*dims, fake, fake, fake, fake, 1 << 40, fake, fake, fake, None) == code
 
 
 def _fwd_args(dims, ptrs, saved_bytes):
@@ -116,3 +118,21 @@ def test_bwd_argument_checks(L):
     assert L.mamba2_scan_bwd_reduce(*dims, g, ws, None, g, g, None) == m2.ENULL
     assert L.mamba2_scan_bwd_reduce(*dims, g, ws - 4, g, g, g, None) == m2.ESIZE
     assert L.mamba2_scan_bwd_reduce(*dims, ctypes.c_void_p(0x20004), ws, g, g, g, None) == m2.EALIGN
+
+
+def test_bwd_input_argument_checks(L):
+    dims = (100, 5, 192, 32)
+    sv = m2.saved_bytes(*dims)
+    g = ctypes.c_void_p(0x30000)
+
+    def call(wa=g, wb=g, wc=g, saved=g, svb=sv, dctx=g, dh=g, dhs=g):
+        return L.mamba2_scan_bwd_input(*dims, wa, wb, wc, saved, svb, dctx, dh, dhs, None)
+
+    for kw in ("wa", "wb", "wc", "saved", "dctx"):
+        assert call(**{kw: None}) == m2.ENULL, kw
+    assert call(dh=None, dhs=None) == m2.ENULL
+    assert call(svb=sv - 4) == m2.ESIZE
+    for kw, off in (("wa", 2), ("wb", 1), ("wc", 3), ("dctx", 2), ("saved", 4), ("dh", 8), ("dhs", 4)):
+        assert call(**{kw: ctypes.c_void_p(0x30000 + off)}) == m2.EALIGN, kw
+    # one output may be NULL (and then is not checked for alignment)
+    assert call(dh=None, dhs=ctypes.c_void_p(0x30000 + 4)) == m2.EALIGN
