@@ -47,6 +47,7 @@
 #include "mamba2_scan.h"
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -580,99 +581,268 @@ __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
 //   d_h_s2[b][j]         = sum_s d_c[b,s]   W_C[j][s]
 // with d_a, d_b, d_c formed from `saved` and d_context exactly as in the
 // backward.  Neither h_history nor h_s2 is read.
-//   grid = 8 * (SH2/64) * ceil(NB / 8), 512 threads.  Work-group: (16-sample
-//   block, 64-feature column block), the column blocks of one sample block on
-//   one XCD so they share the saved planes in L2.  Waves take units u = 0..K
-//   (history step u, or the readout when u = K) round-robin.
+//   grid = 8 * (SH2/64) * ceil(NCH / 8), 256 threads.  Work-group: a chunk of
+//   BPW consecutive 16-sample blocks and one 64-feature column block; the
+//   column blocks of a chunk run on one XCD so they share the saved planes
+//   in L2.  A unit is (sample block, step t) for t < K, or the readout
+//   (t = K); wave w takes units w, w+4, ... of its work-group and requests
+//   the next unit's operands while it multiplies the current one.
+// Operands: a unit's saved planes and the block's d_context arrive as whole
+// 1 KiB rows (one 16-byte load per lane each, four per unit at D = 16) and
+// pass through the wave's LDS tile into the MFMA layout.  The kernel writes
+// eight times what it reads, so every load waits behind queued stores in
+// the CU's memory pipeline; few, wide loads keep that pipeline short.
 // MFMA roles: M = 16 features (4 tiles), N = the 16 samples, K = the 2*D
-// (or D) states.  A lane (kg, m): W[feature m][state 4q+kg] from the
-// work-group's LDS copy of the column block's weights; B lane (kg, n):
-// d[sample n][state 4q+kg] from a per-wave LDS tile.  A result lane then
-// holds 4 consecutive features of one sample: one 16-byte store.
+// (or D) states, in the order described at DinW; B lane (kg, n) holds
+// d[sample n][the same state] from the tile.  Results leave
+// through the wave's LDS tile as 256-byte row pieces (stores in 64-byte
+// pieces fall well short of the HBM write rate).
+// Every unit issues the same loads (a readout loads x_K where a step loads
+// alpha' and beta') and the same four stores, range-checked by a buffer
+// descriptor rather than by a branch, so the compiler's memory-counter waits
+// stay exact and the next unit's requests stay in flight.
+constexpr int kDinWaves = 4;
+constexpr int kDinTargetWGs = 4096 / kDinWaves;      // 16 resident waves per CU
+constexpr int kDinRow = kColBlock + 4;               // padded LDS row of the output transpose
+constexpr int kDinPlaneLds = kPlane + 16;            // padded LDS copy of a saved plane
+constexpr unsigned kBufWord3 = 0x00020000u;          // gfx9 buffer descriptor: 32-bit data format
+constexpr long long kDinMaxRowFloats = 1LL << 26;    // K * SH2 limit: 16 rows of samples stay below 4 GiB
+
+// LDS floats of one wave's tile: the unit's planes (alpha', beta', S_r,
+// d_context; NGT of each), reused afterwards for the output transpose.
+__host__ __device__ constexpr int din_tile_floats(int ngt) {
+  return 4 * ngt * kDinPlaneLds > kBlock * kDinRow ? 4 * ngt * kDinPlaneLds : kBlock * kDinRow;
+}
+
 template <int NGT>
-__global__ __launch_bounds__(kFwdWaves * 64) void dinput_kernel(
-    int B, int K, int SH2, int NB,
+struct DinUnit {
+  v4f pa[NGT];  // alpha'_t (step) or x_K (readout) plane of each state group
+  v4f pb[NGT];  // beta'_t (step) or x_K again (readout)
+  v4f ps[NGT];  // S_r plane of the step's round (multi-round histories only)
+  v4f pd[NGT];  // the block's d_context rows, sample-major
+};
+
+struct DinCtx {
+  int B, K, blk0;
+  size_t blk_stride;
+  const float* saved;
+  const float* dctx;
+};
+
+template <int NGT, bool ROUNDS>
+__device__ __forceinline__ void din_load(DinUnit<NGT>& U, int u, const DinCtx& c, int lane) {
+  constexpr int D = NGT * kGroup;
+  const int KU = c.K + 1;
+  const int bi = u / KU;
+  const int t = u - bi * KU;
+  const int blk = c.blk0 + bi;
+  const bool step = t < c.K;
+  const int p0 = step ? 2 * t : 2 * c.K;
+  const int p1 = step ? 2 * t + 1 : 2 * c.K;
+  const int ps = 2 * c.K + 1 + (step ? t / kChunk : 0);
+  const float* sv = c.saved + (size_t)blk * NGT * c.blk_stride + 4 * lane;
+  // d_context rows of the block; rows past B are clamped to row B-1 (their
+  // results are never stored)
+  const int nrow = c.B - blk * kBlock;
+  const float* dc = c.dctx + (size_t)blk * kBlock * D;
+#pragma unroll
+  for (int g = 0; g < NGT; ++g) {
+    const float* gp = sv + (size_t)g * c.blk_stride;
+    U.pa[g] = ld4(gp + (size_t)p0 * kPlane);
+    U.pb[g] = ld4(gp + (size_t)p1 * kPlane);
+    if (ROUNDS) U.ps[g] = ld4(gp + (size_t)ps * kPlane);
+    const int e = (g * 64 + lane) * 4;  // float index in the block's [16][D] rows
+    const int row = min(e / D, nrow - 1);
+    U.pd[g] = ld4(dc + (size_t)row * D + (e % D));
+  }
+}
+
+// The column block's weights as MFMA A operands.  Contraction element of
+// q-step q for lane kg: kappa = 16*(q/4) + 4*kg + q%4 (kappa < D: state kappa
+// of W_A; kappa >= D: state kappa - D of W_B), so the four q-steps 4qq..4qq+3
+// of lane (kg, m) are one contiguous float4 of a W row, staged in the
+// work-group's LDS.  (Holding them in registers instead, at D = 16, was no
+// faster.)
+__device__ __forceinline__ const float* din_w_src(const float* WA, const float* WB, int NGT, int qq) {
+  return qq < NGT ? WA : WB;
+}
+
+template <int NGT>
+struct DinW {
+  const float* sab;  // [jt][qq][lane] float4
+  const float* sc;
+  int lane;
+  __device__ __forceinline__ v4f AB(int jt, int qq) const {
+    return *reinterpret_cast<const v4f*>(&sab[((jt * 2 * NGT + qq) * 64 + lane) * 4]);
+  }
+  __device__ __forceinline__ v4f C(int jt, int qq) const {
+    return *reinterpret_cast<const v4f*>(&sc[((jt * NGT + qq) * 64 + lane) * 4]);
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t din_rsrc(float* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufWord3);
+}
+
+template <int NGT, bool ROUNDS, class WOps>
+__device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const DinCtx& c, int SH2, int jb, int kg,
+                                            int n, const WOps& W, float* __restrict__ tile, int lane,
+                                            float* __restrict__ dH, float* __restrict__ dhs2) {
+  constexpr int D = NGT * kGroup;
+  constexpr int NQ = D / 4;
+  const int KU = c.K + 1;
+  const int bi = u / KU;
+  const int t = u - bi * KU;
+  const int blk = c.blk0 + bi;
+  const bool readout = t == c.K;
+
+  // operands into the tile: [kind][group] planes, then the d_context rows
+  float* tA = tile;
+  float* tB = tile + NGT * kDinPlaneLds;
+  float* tS = tile + 2 * NGT * kDinPlaneLds;
+  float* tD = tile + 3 * NGT * kDinPlaneLds;
+#pragma unroll
+  for (int g = 0; g < NGT; ++g) {
+    *reinterpret_cast<v4f*>(&tA[g * kDinPlaneLds + 4 * lane]) = U.pa[g];
+    *reinterpret_cast<v4f*>(&tB[g * kDinPlaneLds + 4 * lane]) = U.pb[g];
+    if (ROUNDS) *reinterpret_cast<v4f*>(&tS[g * kDinPlaneLds + 4 * lane]) = U.ps[g];
+    *reinterpret_cast<v4f*>(&tD[(g * 64 + lane) * 4]) = U.pd[g];
+  }
+  __builtin_amdgcn_wave_barrier();
+  // B operands: lane (kg, n) at q-step i holds state 16(i/4) + 4kg + i%4 of
+  // sample n (d_a for q-step i, d_b for q-step i + NQ)
+  float da[NQ], db[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int sn = 4 * kg + (i & 3);
+    const int pidx = (i >> 2) * kDinPlaneLds + plane_index(n, sn);
+    float dc = tD[n * D + 16 * (i >> 2) + sn];
+    if (ROUNDS && !readout) dc *= tS[pidx];
+    da[i] = dc * tA[pidx];
+    db[i] = dc * tB[pidx];
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  v4f acc[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) acc[jt] = v4f{0.f, 0.f, 0.f, 0.f};
+  if (!readout) {
+    // q-steps 0..NQ-1 contract d_a with W_A, NQ..2NQ-1 d_b with W_B
+#pragma unroll
+    for (int qq = 0; qq < 2 * NQ / 4; ++qq) {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const v4f w = W.AB(jt, qq);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = 4 * qq + i;
+          acc[jt] = mfma16x16x4(w[i], q < NQ ? da[q] : db[q - NQ], acc[jt]);
+        }
+      }
+    }
+  } else {
+    // readout: da holds d_c = d_context * x_K
+#pragma unroll
+    for (int qq = 0; qq < NQ / 4; ++qq) {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const v4f w = W.C(jt, qq);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[jt] = mfma16x16x4(w[i], da[4 * qq + i], acc[jt]);
+      }
+    }
+  }
+  // Result lane (kg, n), element r: feature jt*16 + 4kg + r of the column
+  // block, sample n.  Transposed through the tile so that lane (kg, n) then
+  // stores features 4n..4n+3 of samples 4i+kg, i = 0..3.
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) *reinterpret_cast<v4f*>(&tile[n * kDinRow + jt * 16 + 4 * kg]) = acc[jt];
+  __builtin_amdgcn_wave_barrier();
+  // Descriptor based at (first sample of the block, this unit's row, column
+  // block); its size ends after the last valid sample's 64 features, so the
+  // rows of samples >= B (and every store, for an output not requested) are
+  // dropped by the range check.
+  const int nvalid = min(kBlock, c.B - blk * kBlock);
+  float* out = readout ? dhs2 : dH;
+  const size_t row_stride = readout ? (size_t)SH2 : (size_t)c.K * SH2;  // floats between samples
+  float* base = out == nullptr ? nullptr
+                               : out + (size_t)blk * kBlock * row_stride + (readout ? 0 : (size_t)t * SH2) +
+                                     jb * kColBlock;
+  const unsigned bytes =
+      out == nullptr ? 0u : (unsigned)(((size_t)(nvalid - 1) * row_stride + kColBlock) * sizeof(float));
+  const __amdgpu_buffer_rsrc_t rs = din_rsrc(base, bytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v4f v = *reinterpret_cast<const v4f*>(&tile[(4 * i + kg) * kDinRow + 4 * n]);
+    const unsigned off = (unsigned)(((size_t)(4 * i + kg) * row_stride + 4 * n) * sizeof(float));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rs, off, 0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int NGT, bool ROUNDS>
+__global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
+    int B, int K, int SH2, int NB, int BPW,
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
     const float* __restrict__ saved, const float* __restrict__ dctx,
     float* __restrict__ dH, float* __restrict__ dhs2) {
   constexpr int D = NGT * kGroup;
-  constexpr int DP = D + 1;  // padded rows: fewer LDS bank conflicts
-  __shared__ float sW[3][kColBlock][DP];
-  __shared__ float sDc[kBlock][DP];
-  __shared__ float sXk[kBlock][DP];
-  __shared__ float sA[kFwdWaves][kBlock][2 * D + 1];
+  // weights: [tile jt][q-step group qq][lane] float4
+  __shared__ float sWab[4 * 2 * NGT * 64 * 4];
+  __shared__ float sWc[4 * NGT * 64 * 4];
+  __shared__ float sTile[kDinWaves][din_tile_floats(NGT)];
 
   const int NJB = SH2 / kColBlock;
   const int xcd = blockIdx.x & 7;
   const int round = blockIdx.x >> 3;
   const int jb = round % NJB;
-  const int blk = (round / NJB) * 8 + xcd;
-  if (blk >= NB) return;
+  const int chunk = (round / NJB) * 8 + xcd;
+  DinCtx c;
+  c.blk0 = chunk * BPW;
+  if (c.blk0 >= NB) return;
+  c.B = B;
+  c.K = K;
+  c.blk_stride = (size_t)saved_planes(K) * kPlane;
+  c.saved = saved;
+  c.dctx = dctx;
+  const int n_units = min(BPW, NB - c.blk0) * (K + 1);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int kg = lane >> 4;
-  const int m = lane & 15;
-  const bool rounds = K > kChunk;
-  const size_t blk_stride = (size_t)saved_planes(K) * kPlane;
+  const int n = lane & 15;
 
-  for (int e = tid; e < 3 * kColBlock * D; e += kFwdWaves * 64) {
-    const int mat = e / (kColBlock * D), r = e - mat * (kColBlock * D);
-    const int jl = r / D, st = r - jl * D;
-    const float* W = mat == 0 ? WA : (mat == 1 ? WB : WC);
-    sW[mat][jl][st] = W[(size_t)(jb * kColBlock + jl) * D + st];
+  // The first unit's operands go out before the weights.
+  constexpr int S = kDinWaves;
+  DinUnit<NGT> R0, R1;
+  din_load<NGT, ROUNDS>(R0, min(wave, n_units - 1), c, lane);
+
+  for (int e = tid; e < 4 * 2 * NGT * 64; e += kDinWaves * 64) {
+    const int l = e & 63, qq = (e >> 6) % (2 * NGT), jt = (e >> 6) / (2 * NGT);
+    const size_t row = (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * D + 4 * (l >> 4);
+    *reinterpret_cast<v4f*>(&sWab[e * 4]) = ld4(din_w_src(WA, WB, NGT, qq) + row + 16 * (qq % NGT));
   }
-  for (int e = tid; e < kBlock * D; e += kFwdWaves * 64) {
-    const int sl = e / D, st = e - sl * D;
-    const int b = blk * kBlock + sl;
-    sDc[sl][st] = b < B ? dctx[(size_t)b * D + st] : 0.f;
-    sXk[sl][st] = saved[((size_t)blk * NGT + st / kGroup) * blk_stride + (size_t)(2 * K) * kPlane +
-                        plane_index(sl, st % kGroup)];
+  for (int e = tid; e < 4 * NGT * 64; e += kDinWaves * 64) {
+    const int l = e & 63, qq = (e >> 6) % NGT, jt = (e >> 6) / NGT;
+    const size_t row = (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * D + 4 * (l >> 4);
+    *reinterpret_cast<v4f*>(&sWc[e * 4]) = ld4(WC + row + 16 * qq);
   }
+  DinW<NGT> W;
+  W.sab = sWab;
+  W.sc = sWc;
+  W.lane = lane;
   __syncthreads();
 
-  for (int u = wave; u <= K; u += kFwdWaves) {
-    const bool readout = (u == K);
-    if (readout ? dhs2 == nullptr : dH == nullptr) continue;
-    // this wave's A tile: d_a | d_b (or d_c) of the block's 16 samples
-    for (int e = lane; e < kBlock * D; e += 64) {
-      const int sl = e / D, st = e - sl * D;
-      if (readout) {
-        sA[wave][sl][st] = sDc[sl][st] * sXk[sl][st];
-      } else {
-        const float* sv = saved + ((size_t)blk * NGT + st / kGroup) * blk_stride;
-        const int pi = plane_index(sl, st % kGroup);
-        float dc = sDc[sl][st];
-        if (rounds) dc *= sv[(size_t)(2 * K + 1 + u / kChunk) * kPlane + pi];
-        sA[wave][sl][st] = dc * sv[(size_t)(2 * u) * kPlane + pi];
-        sA[wave][sl][D + st] = dc * sv[(size_t)(2 * u + 1) * kPlane + pi];
-      }
-    }
-    // The tile is written and read by this wave only, and a wave's LDS
-    // operations complete in order; keep the compiler from moving reads up.
-    __builtin_amdgcn_wave_barrier();
-    v4f acc[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) acc[jt] = v4f{0.f, 0.f, 0.f, 0.f};
-    const int steps = readout ? D / 4 : 2 * D / 4;
-    for (int q = 0; q < steps; ++q) {
-      const int k = 4 * q + kg;
-      const float d = sA[wave][m][k];
-      const int mat = readout ? 2 : (4 * q < D ? 0 : 1);
-      const int st = (readout || 4 * q < D) ? k : k - D;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) acc[jt] = mfma16x16x4(sW[mat][jt * 16 + m][st], d, acc[jt]);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // result lane (g, n), element r: feature jb*64 + jt*16 + 4g + r, sample n
-    const int b = blk * kBlock + m;
-    if (b < B) {
-      float* dst = readout ? dhs2 + (size_t)b * SH2 : dH + ((size_t)b * K + u) * SH2;
-      dst += jb * kColBlock + 4 * kg;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) st4_stream(dst + jt * 16, acc[jt]);
-    }
+  // Two-unit ring; a request past the last unit re-loads the last unit (unused).
+  for (int u = wave; u < n_units; u += 2 * S) {
+    din_load<NGT, ROUNDS>(R1, min(u + S, n_units - 1), c, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    din_compute<NGT, ROUNDS>(R0, u, c, SH2, jb, kg, n, W, sTile[wave], lane, dH, dhs2);
+    if (u + S >= n_units) break;
+    din_load<NGT, ROUNDS>(R0, min(u + 2 * S, n_units - 1), c, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    din_compute<NGT, ROUNDS>(R1, u + S, c, SH2, jb, kg, n, W, sTile[wave], lane, dH, dhs2);
   }
 }
 
@@ -761,12 +931,26 @@ void launch_reduce(const Plan& pl, const void* ws, float* dWA, float* dWB, float
                      static_cast<const float*>(ws), dWA, dWB, dWC);
 }
 
+// Chunk size: about kDinTargetWGs work-groups over all chunks and column blocks.
+int dinput_bpw(const Plan& pl) {
+  const long long units = (long long)pl.NB * pl.NJB * (pl.K + 1);
+  const long long per_wg = (units + kDinTargetWGs - 1) / kDinTargetWGs;
+  long long bpw = (per_wg + pl.K) / (pl.K + 1);
+  return (int)(bpw < 1 ? 1 : (bpw > pl.NB ? pl.NB : bpw));
+}
+
 template <int NGT>
 void launch_dinput(const Plan& pl, const float* WA, const float* WB, const float* WC, const float* sv,
                    const float* dctx, float* dH, float* dhs2, hipStream_t st) {
-  const int grid = 8 * pl.NJB * ((pl.NB + 7) / 8);
-  hipLaunchKernelGGL(dinput_kernel<NGT>, dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NB, WA,
-                     WB, WC, sv, dctx, dH, dhs2);
+  const int bpw = dinput_bpw(pl);
+  const int nch = (pl.NB + bpw - 1) / bpw;
+  const int grid = 8 * pl.NJB * ((nch + 7) / 8);
+  if (pl.K > kChunk)
+    hipLaunchKernelGGL((dinput_kernel<NGT, true>), dim3(grid), dim3(kDinWaves * 64), 0, st, pl.B, pl.K, pl.SH2,
+                       pl.NB, bpw, WA, WB, WC, sv, dctx, dH, dhs2);
+  else
+    hipLaunchKernelGGL((dinput_kernel<NGT, false>), dim3(grid), dim3(kDinWaves * 64), 0, st, pl.B, pl.K, pl.SH2,
+                       pl.NB, bpw, WA, WB, WC, sv, dctx, dH, dhs2);
 }
 
 }  // namespace
@@ -861,6 +1045,8 @@ int mamba2_scan_bwd_input(int B, int K, int SH2, int STATE_D, const float* W_A, 
   Plan pl;
   int st = make_plan(B, K, SH2, STATE_D, &pl);
   if (st != MAMBA2_SCAN_OK) return st;
+  // a 16-sample block's rows must span less than 4 GiB (32-bit store offsets)
+  if ((long long)K * SH2 > kDinMaxRowFloats) return MAMBA2_SCAN_EUNSUPPORTED;
   if (!W_A || !W_B || !W_C || !saved || !d_context || (!d_h_history && !d_h_s2)) return MAMBA2_SCAN_ENULL;
   if (saved_bytes < pl.saved_bytes) return MAMBA2_SCAN_ESIZE;
   if (!aligned16(saved) || !aligned4(W_A) || !aligned4(W_B) || !aligned4(W_C) || !aligned4(d_context) ||

@@ -140,6 +140,7 @@ int mamba2_scan_bwd_reduce(int B, int K, int SH2, int STATE_D,
  * device memory, 16-byte aligned); either may be NULL to skip it, not both.
  * Independent of mamba2_scan_bwd: the two may run in either order or on
  * different streams once the forward has finished.
+ * Supports K * SH2 <= 2^26 (MAMBA2_SCAN_EUNSUPPORTED beyond).
  * Returns MAMBA2_SCAN_ENULL for a NULL input or both outputs NULL,
  * MAMBA2_SCAN_ESIZE if saved_bytes is short, MAMBA2_SCAN_EALIGN for a
  * misaligned pointer (saved, d_h_history, d_h_s2: 16 bytes; the rest: 4).

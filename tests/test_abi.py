@@ -136,3 +136,5 @@ def test_bwd_input_argument_checks(L):
         assert call(**{kw: ctypes.c_void_p(0x30000 + off)}) == m2.EALIGN, kw
     # one output may be NULL (and then is not checked for alignment)
     assert call(dh=None, dhs=ctypes.c_void_p(0x30000 + 4)) == m2.EALIGN
+    # a 16-sample block of d_h_history rows must stay under 4 GiB (K * SH2 <= 2^26)
+    assert L.mamba2_scan_bwd_input(1, 1 << 18, 512, 16, g, g, g, g, 1 << 40, g, g, g, None) == m2.EUNSUPPORTED
