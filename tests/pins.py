@@ -294,6 +294,105 @@ def check_input_grads_finite_difference(orc):
             assert err <= 2e-8 * max(1.0, float(np.max(np.abs(an)))), ((B, K, SH2, D), err)
 
 
+# ------------------------------------------- stability multiplier and blend
+def check_stability_geometric(orc):
+    """W_A = 0 gives sigma = 1/2; with multiplier m the gate is m/2.
+
+    Rows equal across t give b_t = beta (an integer), so with m = 1/2:
+    x_K = beta * sum_{i<K} 4^-i exactly, and context = c * x_K exactly.  With
+    m = 0 only the newest input survives: x_K = b_{K-1}.  (A multiplier that
+    scaled the input instead of the gate would give beta * sum 2^-i * 1/2.)
+    """
+    rng = np.random.default_rng(1111)
+    B, K, SH2, D = 3, 6, 5, 2
+    H, h_s2, W_A, W_B, W_C = _int_inputs(rng, B, K, SH2, D)
+    W_A[:] = 0.0
+    Heq = np.repeat(H[:, :1], K, axis=1)
+    f = orc.forward(Heq, h_s2, W_A, W_B, W_C, stability=0.5)
+    geo = sum(Fraction(1, 4 ** i) for i in range(K))
+    for b in range(B):
+        for s in range(D):
+            beta = _dot_int(Heq[b, 0], W_B[:, s])
+            c = _dot_int(h_s2[b], W_C[:, s])
+            assert f.x[b, K, s] == float(beta * geo), (b, s)
+            assert f.context[b, s] == float(c * beta * geo), (b, s)
+    f0 = orc.forward(H, h_s2, W_A, W_B, W_C, stability=0.0)
+    for b in range(B):
+        for s in range(D):
+            assert f0.x[b, K, s] == _dot_int(H[b, K - 1], W_B[:, s]), (b, s)
+
+
+def check_stability_backward_products(orc):
+    """Reverse scan with multiplier m, by products: d_b[t] = d_context c prod_{u>t} m g_u,
+    d_a[t] = d_b[t] x_t m g_t (1 - g_t), with g = scipy expit of the oracle's logits."""
+    rng = np.random.default_rng(1212)
+    B, K, SH2, D = 3, 5, 4, 3
+    H, h_s2, W_A, W_B, W_C, d_ctx = _real_inputs(rng, B, K, SH2, D, wa_scale=1.0)
+    m = 0.7
+    f = orc.forward(H, h_s2, W_A, W_B, W_C, stability=m)
+    g = orc.backward(f, H, h_s2, d_ctx)
+    gate = expit(f.a)
+    # the forward itself, by the same closed form: x_{t+1} = m g_t x_t + b_t
+    x = np.zeros((B, D))
+    for t in range(K):
+        x = m * gate[:, t] * x + f.bb[:, t]
+    np.testing.assert_allclose(f.x[:, K], x, rtol=1e-13, atol=1e-14)
+    for t in range(K):
+        suffix = np.prod(m * gate[:, t + 1:], axis=1) if t + 1 < K else np.ones((B, D))
+        db = d_ctx * f.c * suffix
+        np.testing.assert_allclose(g.d_b[:, t], db, rtol=1e-13, atol=1e-15)
+        da = db * f.x[:, t] * m * gate[:, t] * (1 - gate[:, t])
+        np.testing.assert_allclose(g.d_a[:, t], da, rtol=1e-12, atol=1e-15)
+
+
+def check_blend_closed_form(orc):
+    """K = 1, integer inputs, D = 4: h_enriched = h_s2 + w * (sum_s c x_1) / 4, exactly.
+
+    x_1 = b_0, every product and the division by a power of two are exact in
+    float64.  Also w absent means w = 1.
+    """
+    rng = np.random.default_rng(1313)
+    B, K, SH2, D = 3, 1, 5, 4
+    H, h_s2, W_A, W_B, W_C = _int_inputs(rng, B, K, SH2, D)
+    w = rng.integers(-3, 4, SH2).astype(np.float64)
+    f = orc.forward(H, h_s2, W_A, W_B, W_C)
+    he = orc.blend(f.context, h_s2, w)
+    he1 = orc.blend(f.context, h_s2)
+    for b in range(B):
+        tot = sum(_dot_int(h_s2[b], W_C[:, s]) * _dot_int(H[b, 0], W_B[:, s]) for s in range(D))
+        for j in range(SH2):
+            assert he[b, j] == float(Fraction(int(h_s2[b, j])) + int(w[j]) * Fraction(tot, D)), (b, j)
+            assert he1[b, j] == float(Fraction(int(h_s2[b, j])) + Fraction(tot, D)), (b, j)
+
+
+def check_blend_finite_difference(orc):
+    """Central differences of L = sum(d_h_enriched * h_enriched) through the blend.
+
+    With a stability multiplier (0.8, 1.3) and temporal weights (random, or
+    absent): every entry of W_A, W_B, W_C, the temporal weights and h_s2 (whose
+    gradient is the residual plus the W_C path).  h = 1e-6.
+    """
+    rng = np.random.default_rng(1414)
+    for (B, K, SH2, D), m, with_w in (((3, 4, 5, 2), 0.8, True), ((2, 7, 3, 4), 1.3, False)):
+        H, h_s2, W_A, W_B, W_C, _ = _real_inputs(rng, B, K, SH2, D, wa_scale=1.0)
+        w = rng.uniform(0.5, 1.5, SH2) if with_w else None
+        dhe = rng.standard_normal((B, SH2))
+        inp = dict(h_history=H, h_s2=h_s2, W_A=W_A, W_B=W_B, W_C=W_C, d_h_enriched=dhe)
+        _, _, bb, b = orc.fwd_bwd_blend(inp, m, w)
+        d_hs2 = bb.d_h_s2_residual + orc.input_grads(b, W_A, W_B, W_C).d_h_s2
+
+        def L():
+            return orc.loss_blend(H, h_s2, W_A, W_B, W_C, dhe, m, w)
+
+        checks = [(W_A, b.dW_A), (W_B, b.dW_B), (W_C, b.dW_C), (h_s2, d_hs2)]
+        if w is not None:
+            checks.append((w, bb.d_temporal_weight))
+        for X, an in checks:
+            fd = _fd_grad(L, X, 1e-6)
+            err = float(np.max(np.abs(fd - an)))
+            assert err <= 2e-8 * max(1.0, float(np.max(np.abs(an)))), ((B, K, SH2, D), m, err)
+
+
 ALL_PINS = [
     check_k1_closed_form,
     check_half_gate_geometric,
@@ -305,4 +404,8 @@ ALL_PINS = [
     check_k1_no_gate_gradient,
     check_invariants,
     check_input_grads_finite_difference,
+    check_stability_geometric,
+    check_stability_backward_products,
+    check_blend_closed_form,
+    check_blend_finite_difference,
 ]

@@ -21,28 +21,40 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _scan_fwd_time_reversed(a, bb):
+def _scan_fwd_time_reversed(a, bb, m=1.0):
     a, bb = _f64(a), _f64(bb)
     B, K, D = a.shape
     g = orc.logistic(a)
     x = np.zeros((B, K + 1, D))
     for step, t in enumerate(range(K - 1, -1, -1)):
-        x[:, step + 1] = g[:, t] * x[:, step] + bb[:, t]
+        x[:, step + 1] = m * g[:, t] * x[:, step] + bb[:, t]
     return g, x
 
 
-def _scan_fwd_x0_one(a, bb):
+def _scan_fwd_x0_one(a, bb, m=1.0):
     a, bb = _f64(a), _f64(bb)
     B, K, D = a.shape
     g = orc.logistic(a)
     x = np.ones((B, K + 1, D))
     for t in range(K):
-        x[:, t + 1] = g[:, t] * x[:, t] + bb[:, t]
+        x[:, t + 1] = m * g[:, t] * x[:, t] + bb[:, t]
     return g, x
 
 
-def _make_scan_bwd(x_index_shift=0, dx_k_times_c=True, sig_prime=True, carry_gate=True):
-    def scan_backward(g, x, c, d_context):
+def _scan_fwd_stability_on_input(a, bb, m=1.0):
+    # plausible mistake: the multiplier scales the new input instead of the gate
+    a, bb = _f64(a), _f64(bb)
+    B, K, D = a.shape
+    g = orc.logistic(a)
+    x = np.zeros((B, K + 1, D))
+    for t in range(K):
+        x[:, t + 1] = g[:, t] * x[:, t] + m * bb[:, t]
+    return g, x
+
+
+def _make_scan_bwd(x_index_shift=0, dx_k_times_c=True, sig_prime=True, carry_gate=True, m_in_d_a=True,
+                   m_in_carry=True):
+    def scan_backward(g, x, c, d_context, m=1.0):
         g, x, d_context = _f64(g), _f64(x), _f64(d_context)
         B, K, D = g.shape
         dx = d_context * _f64(c) if dx_k_times_c else d_context.copy()
@@ -53,8 +65,8 @@ def _make_scan_bwd(x_index_shift=0, dx_k_times_c=True, sig_prime=True, carry_gat
             gt = g[:, t]
             d_b[:, t] = dx
             sp = gt * (1.0 - gt) if sig_prime else gt
-            d_a[:, t] = dx * x[:, t + x_index_shift] * sp
-            dx = dx * (gt if carry_gate else (1.0 - gt))
+            d_a[:, t] = dx * x[:, t + x_index_shift] * sp * (m if m_in_d_a else 1.0)
+            dx = dx * (gt if carry_gate else (1.0 - gt)) * (m if m_in_carry else 1.0)
         return d_a, d_b, d_c
     return scan_backward
 
@@ -71,10 +83,36 @@ def _backward_swapped_planes(fwd, h_history, h_s2, d_context):
     return b
 
 
-def _forward_sum_readout(h_history, h_s2, W_A, W_B, W_C):
-    f = _ORIG_FORWARD(h_history, h_s2, W_A, W_B, W_C)
+def _forward_sum_readout(h_history, h_s2, W_A, W_B, W_C, stability=1.0):
+    f = _ORIG_FORWARD(h_history, h_s2, W_A, W_B, W_C, stability)
     f.context = f.c + f.x[:, -1]
     return f
+
+
+def _blend_without_mean(context, h_s2, temporal_weight=None):
+    D = _f64(context).shape[1]
+    return _ORIG_BLEND(context, h_s2, temporal_weight) * 1.0 + (D - 1) * (
+        _ORIG_BLEND(context, h_s2, temporal_weight) - _f64(h_s2))
+
+
+def _blend_bwd_first_state_only(d_h_enriched, context, temporal_weight=None):
+    r = _ORIG_BLEND_BWD(d_h_enriched, context, temporal_weight)
+    r.d_context[:, 1:] = 0.0
+    return r
+
+
+def _blend_bwd_weight_without_mean(d_h_enriched, context, temporal_weight=None):
+    r = _ORIG_BLEND_BWD(d_h_enriched, context, temporal_weight)
+    r.d_temporal_weight = r.d_temporal_weight * _f64(context).shape[1]
+    return r
+
+
+def _blend_bwd_ignores_weight(d_h_enriched, context, temporal_weight=None):
+    # plausible mistake: d_context taken as if every temporal weight were 1
+    r = _ORIG_BLEND_BWD(d_h_enriched, context, None)
+    w_r = _ORIG_BLEND_BWD(d_h_enriched, context, temporal_weight)
+    r.d_temporal_weight = w_r.d_temporal_weight
+    return r
 
 
 def _input_grads_wrong_weight(bwd, W_A, W_B, W_C):
@@ -91,6 +129,8 @@ def _input_grads_wrong_weight(bwd, W_A, W_B, W_C):
 _ORIG_BACKWARD = orc.backward
 _ORIG_FORWARD = orc.forward
 _ORIG_INPUT_GRADS = orc.input_grads
+_ORIG_BLEND = orc.blend
+_ORIG_BLEND_BWD = orc.blend_backward
 
 MUTANTS = {
     "gate_sign_flipped": ("logistic", lambda a: 1.0 / (1.0 + np.exp(_f64(a)))),
@@ -106,6 +146,13 @@ MUTANTS = {
     "dWA_dWB_swapped": ("backward", _backward_swapped_planes),
     "readout_added_not_multiplied": ("forward", _forward_sum_readout),
     "input_grad_uses_wrong_weight": ("input_grads", _input_grads_wrong_weight),
+    "stability_scales_input": ("scan_forward", _scan_fwd_stability_on_input),
+    "stability_missing_in_d_a": ("scan_backward", _make_scan_bwd(m_in_d_a=False)),
+    "stability_missing_in_carry": ("scan_backward", _make_scan_bwd(m_in_carry=False)),
+    "blend_sums_instead_of_mean": ("blend", _blend_without_mean),
+    "blend_d_context_first_state_only": ("blend_backward", _blend_bwd_first_state_only),
+    "blend_d_weight_without_mean": ("blend_backward", _blend_bwd_weight_without_mean),
+    "blend_d_context_ignores_weight": ("blend_backward", _blend_bwd_ignores_weight),
 }
 
 
