@@ -9,6 +9,7 @@ The entry points mirror include/mamba2_scan.h:
     bwd(h_history, h_s2, saved, d_context)      -> dict(dW_A, dW_B, dW_C[, d_a, d_b, d_c])
     bwd_partials(...), bwd_reduce(...)          -- the two phases of bwd
     bwd_input(W_A, W_B, W_C, saved, d_context, K) -> (d_h_history, d_h_s2)
+    fwd_blend(...) -> (context, h_enriched, saved);  bwd_blend(...) -> dict(...)
     saved_bytes(B, K, SH2, D), workspace_bytes(B, K, SH2, D)
 """
 from __future__ import annotations
@@ -50,6 +51,9 @@ _SIGNATURES = {
     "mamba2_scan_bwd_partials": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 5 + [_c_size, _c_vp]),
     "mamba2_scan_bwd_reduce": (_c_int, [_c_int] * 4 + [_c_vp, _c_size] + [_c_vp] * 4),
     "mamba2_scan_bwd_input": (_c_int, [_c_int] * 4 + [_c_vp] * 4 + [_c_size] + [_c_vp] * 4),
+    "mamba2_scan_fwd_blend": (_c_int, [_c_int] * 4 + [_c_vp] * 10 + [_c_size, _c_vp]),
+    "mamba2_scan_bwd_blend_workspace_bytes": (_c_size, [_c_int] * 4),
+    "mamba2_scan_bwd_blend": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 8 + [_c_size, _c_vp]),
     "mamba2_scan_strerror": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -269,3 +273,91 @@ def bwd_input(W_A, W_B, W_C, saved, d_context, K, *, d_h_history=None, d_h_s2=No
                                      _ptr(d_context), _ptr(d_h_history), _ptr(d_h_s2), _stream(stream, dev))
     _raise(st, "mamba2_scan_bwd_input")
     return d_h_history, d_h_s2
+
+
+def blend_workspace_bytes(B: int, K: int, SH2: int, D: int) -> int:
+    return int(lib().mamba2_scan_bwd_blend_workspace_bytes(B, K, SH2, D))
+
+
+def fwd_blend(h_history, h_s2, W_A, W_B, W_C, *, stability=None, temporal_weight=None, context=None,
+              h_enriched=None, saved=None, want_h_enriched=True, stream=None):
+    """Forward with the stability multiplier and the h_enriched blend.
+
+    stability: a one-element device tensor (m), or None for 1.
+    Returns (context, h_enriched or None, saved).
+    """
+    torch = _torch()
+    if h_history.dim() != 3 or W_A.dim() != 2:
+        raise ValueError("h_history must be [B, K, SH2] and W_A [SH2, D]")
+    B, K, SH2, D = _dims(h_history, W_A.shape[1])
+    dev = h_history.device
+    _check(h_history, "h_history", (B, K, SH2), None)
+    _check(h_s2, "h_s2", (B, SH2), dev)
+    for name, w in (("W_A", W_A), ("W_B", W_B), ("W_C", W_C)):
+        _check(w, name, (SH2, D), dev)
+    if stability is not None:
+        _check(stability, "stability", None, dev)
+        if stability.numel() < 1:
+            raise ValueError("stability must hold one value")
+    if temporal_weight is not None:
+        _check(temporal_weight, "temporal_weight", (SH2,), dev)
+    if context is None:
+        context = torch.empty((B, D), dtype=torch.float32, device=dev)
+    _check(context, "context", (B, D), dev)
+    if h_enriched is None and want_h_enriched:
+        h_enriched = torch.empty((B, SH2), dtype=torch.float32, device=dev)
+    if h_enriched is not None:
+        _check(h_enriched, "h_enriched", (B, SH2), dev)
+    if saved is None:
+        saved = alloc_saved(B, K, SH2, D, dev)
+    _check(saved, "saved", None, dev)
+    st = lib().mamba2_scan_fwd_blend(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(W_A), _ptr(W_B), _ptr(W_C),
+                                     _ptr(stability), _ptr(temporal_weight), _ptr(context), _ptr(h_enriched),
+                                     _ptr(saved), saved.numel() * 4, _stream(stream, dev))
+    _raise(st, "mamba2_scan_fwd_blend")
+    return context, h_enriched, saved
+
+
+def bwd_blend(h_history, h_s2, saved, d_h_enriched, D, *, temporal_weight=None, want_d_temporal_weight=True,
+              workspace=None, out=None, stream=None):
+    """Backward of the blend and the scan: dict with dW_A, dW_B, dW_C, d_context, d_temporal_weight.
+
+    D is STATE_D (the blend's inputs do not imply it).
+    """
+    torch = _torch()
+    if h_history.dim() != 3 or d_h_enriched.dim() != 2:
+        raise ValueError("h_history must be [B, K, SH2] and d_h_enriched [B, SH2]")
+    B, K, SH2 = (int(v) for v in h_history.shape)
+    dev = h_history.device
+    _check(h_history, "h_history", (B, K, SH2), None)
+    _check(h_s2, "h_s2", (B, SH2), dev)
+    _check(saved, "saved", None, dev)
+    _check(d_h_enriched, "d_h_enriched", (B, SH2), dev)
+    if temporal_weight is not None:
+        _check(temporal_weight, "temporal_weight", (SH2,), dev)
+    D = int(D)
+    if out is None:
+        out = {n: torch.empty((SH2, D), dtype=torch.float32, device=dev) for n in ("dW_A", "dW_B", "dW_C")}
+    for n in ("dW_A", "dW_B", "dW_C"):
+        _check(out[n], n, (SH2, D), dev)
+    res = dict(out)
+    if res.get("d_context") is None:
+        res["d_context"] = torch.empty((B, D), dtype=torch.float32, device=dev)
+    _check(res["d_context"], "d_context", (B, D), dev)
+    if want_d_temporal_weight and res.get("d_temporal_weight") is None:
+        res["d_temporal_weight"] = torch.empty((SH2,), dtype=torch.float32, device=dev)
+    if res.get("d_temporal_weight") is not None:
+        _check(res["d_temporal_weight"], "d_temporal_weight", (SH2,), dev)
+    if workspace is None:
+        n = blend_workspace_bytes(B, K, SH2, D)
+        if n == 0:
+            raise ValueError(f"unsupported dimensions B={B} K={K} SH2={SH2} D={D}")
+        workspace = torch.empty(n // 4, dtype=torch.float32, device=dev)
+    _check(workspace, "workspace", None, dev)
+    st = lib().mamba2_scan_bwd_blend(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(saved), saved.numel() * 4,
+                                     _ptr(temporal_weight), _ptr(d_h_enriched), _ptr(res["d_context"]),
+                                     _ptr(res["dW_A"]), _ptr(res["dW_B"]), _ptr(res["dW_C"]),
+                                     _ptr(res.get("d_temporal_weight")), _ptr(workspace), workspace.numel() * 4,
+                                     _stream(stream, dev))
+    _raise(st, "mamba2_scan_bwd_blend")
+    return res

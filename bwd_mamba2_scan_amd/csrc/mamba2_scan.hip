@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     int B, int K, int NG, int NB,
     const float* __restrict__ H, const float* __restrict__ hs2,
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
-    float* __restrict__ ctx, float* __restrict__ saved) {
+    const float* __restrict__ stab, float* __restrict__ ctx, float* __restrict__ saved) {
   constexpr int SH2 = NKC * 16;
   constexpr int NCR = (NKC + kFwdWaves - 1) / kFwdWaves;                   // readout chunks per wave
   constexpr int PF = kFwdPrefetch < NKC ? kFwdPrefetch : NKC;              // history loads in flight
@@ -218,6 +218,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   const size_t blk_stride = (size_t)saved_planes(K) * kPlane;
   float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
   float x = 0.f, c = 0.f;
+  const float mstab = stab != nullptr ? stab[0] : 1.f;
   float G[kChunk], U[kChunk];
   float Gr[kRegRounds];  // gate product of each round (rounds >= kRegRounds park theirs in saved)
 #pragma unroll
@@ -275,9 +276,11 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
           const float g = __builtin_amdgcn_rcpf(1.f + e);
           // 1 - g, computed without cancellation: e*g = e/(1+e) for a > 0.
           const float omg = a > 0.f ? e * g : 1.f - g;
-          U[tt] = x * g * omg;
-          G[tt] = g;
-          x = g * x + b;
+          // stability multiplier m scales the gate and its derivative (m = 1
+          // leaves every product bit-identical)
+          U[tt] = x * g * omg * mstab;
+          G[tt] = g * mstab;
+          x = G[tt] * x + b;
         }
       }
       // Round-local reverse pass: beta'_t = c * prod of this round's later
@@ -530,35 +533,58 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
 // Backward, phase 2: dW = sum over slices p = 0..P-1, in a fixed order.
 //   grid = ceil(NG * SH2 * 48 / 4 / 32), 256 threads: 32 element quads x 8
 //   contiguous slice groups; the groups are combined in order 0..7.
-__global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
-    int SH2, int NG, int P, const float* __restrict__ ws,
-    float* __restrict__ dWA, float* __restrict__ dWB, float* __restrict__ dWC) {
-  __shared__ v4f sPart[kRedGroups][kRedQuads];
-  const int per_sg = SH2 * 3 * kGroup;
-  const int quads = NG * per_sg / 4;
-  const int ql = threadIdx.x % kRedQuads;
-  const int grp = threadIdx.x / kRedQuads;
-  const int qd = blockIdx.x * kRedQuads + ql;
-  const bool ok = qd < quads;
-  const int e = ok ? qd * 4 : 0;
-  const int sg = e / per_sg;
-  const int o = e - sg * per_sg;
-
+// Fixed-order sum of P slices (stride `stride` floats) of one float4 per
+// thread group: 8 contiguous groups of slices, then the groups in order.
+__device__ __forceinline__ v4f reduce_slices(const float* __restrict__ src, size_t stride, int P, bool ok, int grp,
+                                             int ql, v4f (*sPart)[kRedQuads]) {
   const int pc = (P + kRedGroups - 1) / kRedGroups;
   const int p0 = grp * pc;
   const int p1 = min(P, p0 + pc);
   v4f s = {0.f, 0.f, 0.f, 0.f};
   if (ok) {
-    const float* src = ws + (size_t)sg * P * per_sg + o;
 #pragma unroll 4
-    for (int pp = p0; pp < p1; ++pp) s += ld4(src + (size_t)pp * per_sg);
+    for (int pp = p0; pp < p1; ++pp) s += ld4(src + (size_t)pp * stride);
   }
   sPart[grp][ql] = s;
   __syncthreads();
-  if (grp != 0 || !ok) return;
   v4f tot = sPart[0][ql];
 #pragma unroll
   for (int g = 1; g < kRedGroups; ++g) tot += sPart[g][ql];
+  return tot;
+}
+
+// The dW blocks come first; when dw is given, SH2/128 more blocks sum the
+// blend's d_temporal_weight slices (Pw of SH2 floats at wsw) and scale by 1/D.
+__global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
+    int SH2, int NG, int P, const float* __restrict__ ws,
+    float* __restrict__ dWA, float* __restrict__ dWB, float* __restrict__ dWC,
+    int Pw, const float* __restrict__ wsw, float* __restrict__ dw) {
+  __shared__ v4f sPart[kRedGroups][kRedQuads];
+  const int per_sg = SH2 * 3 * kGroup;
+  const int quads = NG * per_sg / 4;
+  const int dw_blocks = (quads + kRedQuads - 1) / kRedQuads;
+  const int ql = threadIdx.x % kRedQuads;
+  const int grp = threadIdx.x / kRedQuads;
+  const int D = NG * kGroup;
+
+  if ((int)blockIdx.x >= dw_blocks) {
+    const int qd = ((int)blockIdx.x - dw_blocks) * kRedQuads + ql;
+    const bool ok = qd < SH2 / 4;
+    const v4f tot = reduce_slices(wsw + (ok ? 4 * qd : 0), (size_t)SH2, Pw, ok, grp, ql, sPart);
+    if (grp != 0 || !ok) return;
+    const float inv = 1.f / (float)D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dw[4 * qd + r] = tot[r] * inv;
+    return;
+  }
+
+  const int qd = blockIdx.x * kRedQuads + ql;
+  const bool ok = qd < quads;
+  const int e = ok ? qd * 4 : 0;
+  const int sg = e / per_sg;
+  const int o = e - sg * per_sg;
+  const v4f tot = reduce_slices(ws + (size_t)sg * P * per_sg + o, (size_t)per_sg, P, ok, grp, ql, sPart);
+  if (grp != 0 || !ok) return;
 
   const int jb = o / (3 * kColBlock * kGroup);
   const int rem = o - jb * (3 * kColBlock * kGroup);
@@ -566,13 +592,108 @@ __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
   const int rem2 = rem - pl * (kColBlock * kGroup);
   const int jl = rem2 / kGroup;
   const int n = rem2 - jl * kGroup;  // multiple of 4
-  const int D = NG * kGroup;
   float* dst = (pl == 0 ? dWA : (pl == 1 ? dWB : dWC)) + (size_t)(jb * kColBlock + jl) * D + sg * kGroup + n;
   dst[0] = tot[0];
   dst[1] = tot[1];
   dst[2] = tot[2];
   dst[3] = tot[3];
 }
+
+// ---------------------------------------------------------------------------
+// The h_enriched blend, the step after the path (implementation plan, Task 1
+// step 3): h_enriched[b][j] = h_s2[b][j] + w_j * (sum_s context[b][s]) / D
+// with w = temporal_weight (1 for every feature when absent).  Its backward,
+// by the chain rule: dL/d(sum_s context[b][s]) = (d_h_enriched[b,:] . w) / D
+// is every state's d_context, and d_temporal_weight[j] =
+// sum_b d_h_enriched[b][j] (sum_s context[b][s]) / D.  One wave per sample
+// row; a lane holds features 4l..4l+3 (and 256 + 4l.. when SH2 > 256).
+constexpr int kBlendWaves = 8;
+constexpr int kBlendSlices = 256;  // most d_temporal_weight slices (one per backward work-group)
+
+__device__ __forceinline__ float wave_sum(float v) {
+  // butterfly over the 64 lanes: the same fixed order on every call
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kBlendWaves * 64) void blend_fwd_kernel(
+    int B, int SH2, int D, const float* __restrict__ ctx, const float* __restrict__ hs2,
+    const float* __restrict__ w, float* __restrict__ he) {
+  const int b = blockIdx.x * kBlendWaves + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const int lane = threadIdx.x & 63;
+  float sum = 0.f;
+  for (int s = 0; s < D; ++s) sum += ctx[(size_t)b * D + s];  // states in order
+  const float scale = sum * (1.f / (float)D);                  // exact: D is a power of two
+  for (int j = 4 * lane; j < SH2; j += 256) {
+    const v4f h = ld4(hs2 + (size_t)b * SH2 + j);
+    const v4f wv = w != nullptr ? ld4(w + j) : v4f{1.f, 1.f, 1.f, 1.f};
+    v4f o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = h[r] + wv[r] * scale;
+    *reinterpret_cast<v4f*>(he + (size_t)b * SH2 + j) = o;
+  }
+}
+
+//   grid = ceil(B / RPW), 512 threads: work-group p takes samples
+//   [p*RPW, (p+1)*RPW), wave w every 8th of them; it writes every state's
+//   d_context of its samples and slice p of d_temporal_weight (before the
+//   1/D), the waves' partials summed in wave order.  sum_s context[b][s] is
+//   rebuilt from the saved planes: c = beta'_{K-1} (no later gate) and x_K.
+__global__ __launch_bounds__(kBlendWaves * 64) void blend_bwd_kernel(
+    int B, int K, int SH2, int NG, int RPW, const float* __restrict__ saved, const float* __restrict__ w,
+    const float* __restrict__ dhe, float* __restrict__ dctx, float* __restrict__ wpart) {
+  __shared__ v4f sPart[kBlendWaves][128];  // SH2 / 4 <= 128
+  const int p = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int D = NG * kGroup;
+  const size_t blk_stride = (size_t)saved_planes(K) * kPlane;
+  v4f wv[2], acc[2];
+  bool act[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int col = 4 * lane + 256 * r;
+    act[r] = col < SH2;
+    wv[r] = (act[r] && w != nullptr) ? ld4(w + col) : v4f{1.f, 1.f, 1.f, 1.f};
+    acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  const int b0 = p * RPW;
+  const int b1 = min(B, b0 + RPW);
+  for (int b = b0 + wave; b < b1; b += kBlendWaves) {
+    v4f dv[2];
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      dv[r] = act[r] ? ld4(dhe + (size_t)b * SH2 + 4 * lane + 256 * r) : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part += dv[r][q] * wv[r][q];
+    }
+    const float dsum = wave_sum(part) * (1.f / (float)D);
+    if (lane < D) dctx[(size_t)b * D + lane] = dsum;
+    float cx = 0.f;
+    if (lane < D) {
+      const float* sv = saved + ((size_t)(b >> 4) * NG + (lane >> 4)) * blk_stride;
+      const int pi = plane_index(b & 15, lane & 15);
+      cx = sv[(size_t)(2 * K - 1) * kPlane + pi] * sv[(size_t)(2 * K) * kPlane + pi];
+    }
+    const float csum = wave_sum(cx);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) acc[r] += dv[r] * csum;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (act[r]) sPart[wave][lane + 64 * r] = acc[r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < SH2 / 4; e += kBlendWaves * 64) {
+    v4f t = sPart[0][e];
+#pragma unroll
+    for (int v = 1; v < kBlendWaves; ++v) t += sPart[v][e];
+    *reinterpret_cast<v4f*>(wpart + (size_t)p * SH2 + 4 * e) = t;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Input gradients, an optional step past the pages' path (their backward
 // ends with the weight gradients).  By the chain rule through the three
@@ -891,10 +1012,10 @@ int launch_status() {
 
 template <int NKC>
 void launch_fwd(const Plan& pl, const float* H, const float* hs2, const float* WA, const float* WB,
-                const float* WC, float* ctx, float* saved, hipStream_t st) {
+                const float* WC, const float* stab, float* ctx, float* saved, hipStream_t st) {
   const int grid = 8 * pl.NG * ((pl.NB + 7) / 8);
   hipLaunchKernelGGL(fwd_kernel<NKC>, dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
-                     hs2, WA, WB, WC, ctx, saved);
+                     hs2, WA, WB, WC, stab, ctx, saved);
 }
 
 int check_bwd_common(const Plan& pl, const float* H, const float* hs2, const void* saved, size_t saved_bytes,
@@ -924,11 +1045,59 @@ void launch_partials(const Plan& pl, const float* H, const float* hs2, const voi
                      static_cast<float*>(ws));
 }
 
-void launch_reduce(const Plan& pl, const void* ws, float* dWA, float* dWB, float* dWC, hipStream_t st) {
+void launch_reduce(const Plan& pl, const void* ws, float* dWA, float* dWB, float* dWC, hipStream_t st,
+                   int Pw = 0, const float* wsw = nullptr, float* dw = nullptr) {
   const int quads = pl.NG * pl.SH2 * 3 * kGroup / 4;
-  const int grid = (quads + kRedQuads - 1) / kRedQuads;
+  int grid = (quads + kRedQuads - 1) / kRedQuads;
+  if (dw != nullptr) grid += (pl.SH2 / 4 + kRedQuads - 1) / kRedQuads;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, st, pl.SH2, pl.NG, pl.P,
-                     static_cast<const float*>(ws), dWA, dWB, dWC);
+                     static_cast<const float*>(ws), dWA, dWB, dWC, Pw, wsw, dw);
+}
+
+int check_fwd(const Plan& pl, const float* H, const float* hs2, const float* WA, const float* WB, const float* WC,
+              const float* ctx, const void* saved, size_t saved_bytes) {
+  if (!H || !hs2 || !WA || !WB || !WC || !ctx || !saved) return MAMBA2_SCAN_ENULL;
+  if (saved_bytes < pl.saved_bytes) return MAMBA2_SCAN_ESIZE;
+  if (!aligned16(H) || !aligned16(hs2) || !aligned16(saved) || !aligned16(WA) || !aligned16(WB) ||
+      !aligned16(WC) || !aligned4(ctx))
+    return MAMBA2_SCAN_EALIGN;
+  return MAMBA2_SCAN_OK;
+}
+
+int run_fwd(const Plan& pl, const float* H, const float* hs2, const float* WA, const float* WB, const float* WC,
+            const float* stab, float* ctx, void* saved, hipStream_t s) {
+  float* sv = static_cast<float*>(saved);
+  switch (pl.SH2 / 64) {
+    case 1: launch_fwd<4>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 2: launch_fwd<8>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 3: launch_fwd<12>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 4: launch_fwd<16>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 5: launch_fwd<20>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 6: launch_fwd<24>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 7: launch_fwd<28>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 8: launch_fwd<32>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    default: return MAMBA2_SCAN_EUNSUPPORTED;
+  }
+  return launch_status();
+}
+
+void launch_blend_fwd(const Plan& pl, const float* ctx, const float* hs2, const float* w, float* he, hipStream_t st) {
+  const int grid = (pl.B + kBlendWaves - 1) / kBlendWaves;
+  hipLaunchKernelGGL(blend_fwd_kernel, dim3(grid), dim3(kBlendWaves * 64), 0, st, pl.B, pl.SH2, pl.D, ctx, hs2, w,
+                     he);
+}
+
+// Samples per blend-backward work-group: a multiple of its 8 waves, so that
+// at most kBlendSlices work-groups (and d_temporal_weight slices) cover B.
+int blend_rows_per_wg(int B) {
+  const int per = (B + kBlendSlices - 1) / kBlendSlices;
+  const int r = ((per + kBlendWaves - 1) / kBlendWaves) * kBlendWaves;
+  return r < kBlendWaves ? kBlendWaves : r;
+}
+
+size_t blend_ws_offset(const Plan& pl) { return (pl.ws_bytes + 255) & ~(size_t)255; }
+size_t blend_ws_bytes(const Plan& pl) {
+  return blend_ws_offset(pl) + (size_t)kBlendSlices * pl.SH2 * sizeof(float);
 }
 
 // Chunk size: about kDinTargetWGs work-groups over all chunks and column blocks.
@@ -973,24 +1142,25 @@ int mamba2_scan_fwd(int B, int K, int SH2, int STATE_D, const float* h_history, 
   Plan pl;
   int st = make_plan(B, K, SH2, STATE_D, &pl);
   if (st != MAMBA2_SCAN_OK) return st;
-  if (!h_history || !h_s2 || !W_A || !W_B || !W_C || !context || !saved) return MAMBA2_SCAN_ENULL;
-  if (saved_bytes < pl.saved_bytes) return MAMBA2_SCAN_ESIZE;
-  if (!aligned16(h_history) || !aligned16(h_s2) || !aligned16(saved) || !aligned16(W_A) || !aligned16(W_B) ||
-      !aligned16(W_C) || !aligned4(context))
-    return MAMBA2_SCAN_EALIGN;
+  st = check_fwd(pl, h_history, h_s2, W_A, W_B, W_C, context, saved, saved_bytes);
+  if (st != MAMBA2_SCAN_OK) return st;
+  return run_fwd(pl, h_history, h_s2, W_A, W_B, W_C, nullptr, context, saved, static_cast<hipStream_t>(stream));
+}
+
+int mamba2_scan_fwd_blend(int B, int K, int SH2, int STATE_D, const float* h_history, const float* h_s2,
+                          const float* W_A, const float* W_B, const float* W_C, const float* stability,
+                          const float* temporal_weight, float* context, float* h_enriched, void* saved,
+                          size_t saved_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_fwd(pl, h_history, h_s2, W_A, W_B, W_C, context, saved, saved_bytes);
+  if (st != MAMBA2_SCAN_OK) return st;
+  if (!aligned4(stability) || !aligned16(temporal_weight) || !aligned16(h_enriched)) return MAMBA2_SCAN_EALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* sv = static_cast<float*>(saved);
-  switch (SH2 / 64) {
-    case 1: launch_fwd<4>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
-    case 2: launch_fwd<8>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
-    case 3: launch_fwd<12>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
-    case 4: launch_fwd<16>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
-    case 5: launch_fwd<20>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
-    case 6: launch_fwd<24>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
-    case 7: launch_fwd<28>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
-    case 8: launch_fwd<32>(pl, h_history, h_s2, W_A, W_B, W_C, context, sv, s); break;
-    default: return MAMBA2_SCAN_EUNSUPPORTED;
-  }
+  st = run_fwd(pl, h_history, h_s2, W_A, W_B, W_C, stability, context, saved, s);
+  if (st != MAMBA2_SCAN_OK || h_enriched == nullptr) return st;
+  launch_blend_fwd(pl, context, h_s2, temporal_weight, h_enriched, s);
   return launch_status();
 }
 
@@ -1036,6 +1206,42 @@ int mamba2_scan_bwd(int B, int K, int SH2, int STATE_D, const float* h_history, 
   st = launch_status();
   if (st != MAMBA2_SCAN_OK) return st;
   launch_reduce(pl, workspace, dW_A, dW_B, dW_C, s);
+  return launch_status();
+}
+
+size_t mamba2_scan_bwd_blend_workspace_bytes(int B, int K, int SH2, int STATE_D) {
+  Plan pl;
+  return make_plan(B, K, SH2, STATE_D, &pl) == MAMBA2_SCAN_OK ? blend_ws_bytes(pl) : 0;
+}
+
+int mamba2_scan_bwd_blend(int B, int K, int SH2, int STATE_D, const float* h_history, const float* h_s2,
+                          const void* saved, size_t saved_bytes, const float* temporal_weight,
+                          const float* d_h_enriched, float* d_context, float* dW_A, float* dW_B, float* dW_C,
+                          float* d_temporal_weight, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  if (!d_h_enriched || !d_context) return MAMBA2_SCAN_ENULL;
+  st = check_bwd_common(pl, h_history, h_s2, saved, saved_bytes, d_context, nullptr, nullptr, nullptr, workspace,
+                        workspace_bytes);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_reduce(pl, workspace, workspace_bytes, dW_A, dW_B, dW_C);
+  if (st != MAMBA2_SCAN_OK) return st;
+  if (workspace_bytes < blend_ws_bytes(pl)) return MAMBA2_SCAN_ESIZE;
+  if (!aligned16(d_h_enriched) || !aligned16(temporal_weight) || !aligned4(d_temporal_weight))
+    return MAMBA2_SCAN_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rpw = blend_rows_per_wg(B);
+  const int pw = (B + rpw - 1) / rpw;
+  float* wsw = reinterpret_cast<float*>(static_cast<char*>(workspace) + blend_ws_offset(pl));
+  hipLaunchKernelGGL(blend_bwd_kernel, dim3(pw), dim3(kBlendWaves * 64), 0, s, B, K, SH2, pl.NG, rpw,
+                     static_cast<const float*>(saved), temporal_weight, d_h_enriched, d_context, wsw);
+  st = launch_status();
+  if (st != MAMBA2_SCAN_OK) return st;
+  launch_partials(pl, h_history, h_s2, saved, d_context, nullptr, nullptr, nullptr, workspace, s);
+  st = launch_status();
+  if (st != MAMBA2_SCAN_OK) return st;
+  launch_reduce(pl, workspace, dW_A, dW_B, dW_C, s, pw, wsw, d_temporal_weight);
   return launch_status();
 }
 

@@ -152,6 +152,57 @@ int mamba2_scan_bwd_input(int B, int K, int SH2, int STATE_D,
                           float* d_h_history, float* d_h_s2,
                           void* stream);
 
+/*
+ * The step after the path, with the stability multiplier (implementation
+ * plan, Task 1 step 3).  As mamba2_scan_fwd, except:
+ *   - the gate is m * sigmoid(a) with m = *stability (a device scalar, such
+ *     as the trainer's isv_signals + 11), or 1 when stability is NULL;
+ *   - when h_enriched [B][SH2] is not NULL it is overwritten with
+ *       h_enriched[b][j] = h_s2[b][j] + w_j * (sum_s context[b][s]) / STATE_D,
+ *     w = temporal_weight [SH2] (all ones when NULL).
+ * `saved` then feeds mamba2_scan_bwd, mamba2_scan_bwd_blend or
+ * mamba2_scan_bwd_input as usual (the multiplier is folded into it).
+ * Alignment: h_enriched and temporal_weight 16 bytes, stability 4 bytes;
+ * the other arguments as for mamba2_scan_fwd.
+ */
+int mamba2_scan_fwd_blend(int B, int K, int SH2, int STATE_D,
+                          const float* h_history, const float* h_s2,
+                          const float* W_A, const float* W_B, const float* W_C,
+                          const float* stability, const float* temporal_weight,
+                          float* context, float* h_enriched,
+                          void* saved, size_t saved_bytes,
+                          void* stream);
+
+/* Bytes of the workspace mamba2_scan_bwd_blend needs; 0 for unsupported dims. */
+size_t mamba2_scan_bwd_blend_workspace_bytes(int B, int K, int SH2, int STATE_D);
+
+/*
+ * Backward of the blend, then of the scan.  The loss is
+ * L = sum_{b,j} d_h_enriched[b][j] * h_enriched[b][j]; by the chain rule
+ *   d_context[b][s] = (sum_j d_h_enriched[b][j] * w_j) / STATE_D for every s,
+ *   d_temporal_weight[j] = sum_b d_h_enriched[b][j] * (sum_s context[b][s]) / STATE_D,
+ * then dW_A, dW_B, dW_C exactly as mamba2_scan_bwd with that d_context.
+ * (The gradient reaching h_s2 through the residual is d_h_enriched itself;
+ * mamba2_scan_bwd_input with the d_context written here adds the W_C path.)
+ * `saved` comes from mamba2_scan_fwd_blend or mamba2_scan_fwd with the same
+ * dimensions, temporal_weight the one the forward used (NULL = ones).
+ * d_context [B][STATE_D] is written (and read back by the scan's backward);
+ * d_temporal_weight [SH2] is overwritten, or skipped when NULL.  workspace:
+ * mamba2_scan_bwd_blend_workspace_bytes() bytes, 16-byte aligned.
+ * Deterministic: bitwise reproducible for given dimensions.
+ * Returns MAMBA2_SCAN_ENULL for a NULL required pointer, MAMBA2_SCAN_ESIZE
+ * for a short saved or workspace, MAMBA2_SCAN_EALIGN for a misaligned one
+ * (d_h_enriched, temporal_weight: 16 bytes).
+ */
+int mamba2_scan_bwd_blend(int B, int K, int SH2, int STATE_D,
+                          const float* h_history, const float* h_s2,
+                          const void* saved, size_t saved_bytes,
+                          const float* temporal_weight, const float* d_h_enriched,
+                          float* d_context, float* dW_A, float* dW_B, float* dW_C,
+                          float* d_temporal_weight,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Static text for a status code. */
 const char* mamba2_scan_strerror(int status);
 

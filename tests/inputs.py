@@ -74,3 +74,16 @@ def make_inputs(B: int, K: int, SH2: int, D: int, seed: int, gate_bias: float = 
 def workload_inputs(name: str):
     w = WORKLOADS[name]
     return make_inputs(w.B, w.K, w.SH2, w.D, w.seed, w.gate_bias)
+
+
+def blend_extras(B: int, SH2: int, seed: int):
+    """Inputs of the h_enriched blend, drawn from their own stream (seed + 1000).
+
+    Draw order: d_h_enriched ~ N(0, 1), shape (B, SH2); temporal_weight ~
+    U(0.5, 1.5), shape (SH2,); both float32.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    return {
+        "d_h_enriched": rng.standard_normal((B, SH2), dtype=np.float32),
+        "temporal_weight": rng.uniform(0.5, 1.5, SH2).astype(np.float32),
+    }

@@ -22,6 +22,7 @@ def test_exports_every_header_symbol(L):
     assert set(names) == {
         "mamba2_scan_saved_bytes", "mamba2_scan_bwd_workspace_bytes", "mamba2_scan_fwd",
         "mamba2_scan_bwd", "mamba2_scan_bwd_partials", "mamba2_scan_bwd_reduce", "mamba2_scan_bwd_input",
+        "mamba2_scan_fwd_blend", "mamba2_scan_bwd_blend_workspace_bytes", "mamba2_scan_bwd_blend",
         "mamba2_scan_strerror",
     }
     for n in names:
@@ -73,6 +74,11 @@ def test_bad_dims(L, dims, code):
                                       fake, 1 << 40, None) == code
     assert L.mamba2_scan_bwd_reduce(*dims, fake, 1 << 40, fake, fake, fake, None) == code
     assert L.mamba2_scan_bwd_input(*dims, fake, fake, fake, fake, 1 << 40, fake, fake, fake, None) == code
+    assert m2.blend_workspace_bytes(*dims) == 0
+    assert L.mamba2_scan_fwd_blend(*dims, fake, fake, fake, fake, fake, None, None, fake, fake, fake, 1 << 40,
+                                   None) == code
+    assert L.mamba2_scan_bwd_blend(*dims, fake, fake, fake, 1 << 40, None, fake, fake, fake, fake, fake, None,
+                                   fake, 1 << 40, None) == code
 
 
 def _fwd_args(dims, ptrs, saved_bytes):
@@ -138,3 +144,44 @@ def test_bwd_input_argument_checks(L):
     assert call(dh=None, dhs=ctypes.c_void_p(0x30000 + 4)) == m2.EALIGN
     # a 16-sample block of d_h_history rows must stay under 4 GiB (K * SH2 <= 2^26)
     assert L.mamba2_scan_bwd_input(1, 1 << 18, 512, 16, g, g, g, g, 1 << 40, g, g, g, None) == m2.EUNSUPPORTED
+
+
+def test_blend_workspace_covers_the_scan_backward():
+    # the blend's workspace holds the scan backward's slices, then at most 256
+    # d_temporal_weight slices of SH2 floats from a 256-byte boundary
+    for B, K, SH2, D in ((64, 8, 256, 16), (8192, 8, 256, 16), (17, 3, 128, 32), (32768, 8, 512, 64)):
+        ws = m2.workspace_bytes(B, K, SH2, D)
+        assert m2.blend_workspace_bytes(B, K, SH2, D) == ((ws + 255) // 256) * 256 + 256 * SH2 * 4
+
+
+def test_fwd_blend_argument_checks(L):
+    dims = (64, 8, 256, 16)
+    need = m2.saved_bytes(*dims)
+    g = ctypes.c_void_p(0x40000)
+
+    def call(h=g, hs=g, wa=g, wb=g, wc=g, stab=None, w=None, ctx=g, he=g, saved=g, svb=need):
+        return L.mamba2_scan_fwd_blend(*dims, h, hs, wa, wb, wc, stab, w, ctx, he, saved, svb, None)
+
+    for kw in ("h", "hs", "wa", "wb", "wc", "ctx", "saved"):
+        assert call(**{kw: None}) == m2.ENULL, kw
+    assert call(svb=need - 4) == m2.ESIZE
+    for kw, off in (("stab", 2), ("w", 4), ("he", 8), ("h", 4)):
+        assert call(**{kw: ctypes.c_void_p(0x40000 + off)}) == m2.EALIGN, kw
+
+
+def test_bwd_blend_argument_checks(L):
+    dims = (100, 5, 192, 32)
+    sv = m2.saved_bytes(*dims)
+    ws = m2.blend_workspace_bytes(*dims)
+    g = ctypes.c_void_p(0x50000)
+
+    def call(h=g, hs=g, saved=g, svb=sv, w=None, dhe=g, dctx=g, dwa=g, dwb=g, dwc=g, dw=None, wk=g, wsb=ws):
+        return L.mamba2_scan_bwd_blend(*dims, h, hs, saved, svb, w, dhe, dctx, dwa, dwb, dwc, dw, wk, wsb, None)
+
+    for kw in ("h", "hs", "saved", "dhe", "dctx", "dwa", "dwb", "dwc", "wk"):
+        assert call(**{kw: None}) == m2.ENULL, kw
+    assert call(svb=sv - 4) == m2.ESIZE
+    assert call(wsb=ws - 4) == m2.ESIZE  # enough for the scan backward, short for the blend's slices
+    assert call(wsb=m2.workspace_bytes(*dims)) == m2.ESIZE
+    for kw, off in (("dhe", 4), ("w", 8), ("dw", 2), ("wk", 4)):
+        assert call(**{kw: ctypes.c_void_p(0x50000 + off)}) == m2.EALIGN, kw
