@@ -39,6 +39,7 @@ MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
 SRC = os.path.join(ROOT, "bwd_mamba2_scan_amd", "csrc", "mamba2_scan.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pages_shape.json")
 MAX_GRAPH_STEPS = 200  # steps per captured graph in the timed region
+BLEND_STABILITY = 0.95  # the blend measurement's gate multiplier
 
 
 def algorithmic_bytes(B, K, SH2, D):
@@ -59,6 +60,10 @@ def algorithmic_bytes(B, K, SH2, D):
         # optional input gradients: read W and d_context, write d_h_history and d_h_s2
         "dinput_kernel": W + vec + H + hs2,
     }
+    # the optional blend step: the scan's bytes plus the h_enriched write (h_s2
+    # is read already), the d_h_enriched read (in place of d_context) and the
+    # temporal weights (read twice, their gradient written)
+    per_kernel["blend_step"] = fwd + bwd + hs2 + hs2 - vec + 3 * SH2 * f
     return fwd + bwd, per_kernel
 
 
@@ -166,7 +171,7 @@ def main():
     import torch
 
     import bwd_mamba2_scan_amd as m2
-    from tests.inputs import WORKLOADS, workload_inputs
+    from tests.inputs import WORKLOADS, blend_extras, workload_inputs
 
     w = WORKLOADS[args.workload]
     B, K, SH2, D = w.B, w.K, w.SH2, w.D
@@ -175,6 +180,7 @@ def main():
     torch.cuda.set_device(dev)
 
     inputs = workload_inputs(args.workload)
+    extras = blend_extras(B, SH2, w.seed)
     base = {k: torch.from_numpy(v).to(dev) for k, v in inputs.items()}
     gate = parity_gate(m2, torch, base, inputs)
 
@@ -189,6 +195,15 @@ def main():
         s["dW"] = [torch.empty((SH2, D), device=dev) for _ in range(3)]
         s["dH"] = torch.empty((B, K, SH2), device=dev)
         s["dhs2"] = torch.empty((B, SH2), device=dev)
+        # the h_enriched blend (an optional step after the path)
+        s["he"] = torch.empty((B, SH2), device=dev)
+        s["dhe"] = torch.from_numpy(extras["d_h_enriched"]).to(dev)
+        s["tw"] = torch.from_numpy(extras["temporal_weight"]).to(dev)
+        s["stab"] = torch.tensor([BLEND_STABILITY], dtype=torch.float32, device=dev)
+        s["bout"] = {"dW_A": torch.empty((SH2, D), device=dev), "dW_B": torch.empty((SH2, D), device=dev),
+                     "dW_C": torch.empty((SH2, D), device=dev), "d_context": torch.empty((B, D), device=dev),
+                     "d_temporal_weight": torch.empty((SH2,), device=dev)}
+        s["bws"] = torch.empty(m2.blend_workspace_bytes(B, K, SH2, D) // 4, device=dev)
         sets.append(s)
     del base
 
@@ -200,6 +215,14 @@ def main():
 
     def reduce(s):
         m2.bwd_reduce(B, K, SH2, D, s["ws"], *s["dW"])
+
+    def fwd_blend(s):
+        m2.fwd_blend(s["h_history"], s["h_s2"], s["W_A"], s["W_B"], s["W_C"], stability=s["stab"],
+                     temporal_weight=s["tw"], context=s["context"], h_enriched=s["he"], saved=s["saved"])
+
+    def bwd_blend(s):
+        m2.bwd_blend(s["h_history"], s["h_s2"], s["saved"], s["dhe"], D, temporal_weight=s["tw"],
+                     workspace=s["bws"], out=s["bout"])
 
     def dinput(s):
         m2.bwd_input(s["W_A"], s["W_B"], s["W_C"], s["saved"], s["d_context"], K, d_h_history=s["dH"],
@@ -329,6 +352,33 @@ def main():
         kern_us[name] = e0.elapsed_time(e1) * 1e3 / n_launch
         del g
 
+    # ---- the blend path (optional step after the path): cold rotation of
+    # fwd_blend(set s) + bwd_blend(set s - R/2), timed like the headline
+    def blend_step(i):
+        fwd_blend(sets[i % R])
+        bwd_blend(sets[(i - R // 2) % R])
+
+    with torch.cuda.stream(stream):
+        for i in range(R):
+            blend_step(i)
+        torch.cuda.synchronize()
+        bg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bg, stream=stream):
+            for i in range(R):
+                blend_step(i)
+        torch.cuda.synchronize()
+        bg.replay()
+        reps = max(2, args.steps // R)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            bg.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    blend_step_us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+    del bg
+
     # ---- copy ceiling: a 1 GiB device-to-device copy (read + write bytes)
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -347,6 +397,7 @@ def main():
     del src, dst
 
     step_bytes, per_kernel_bytes = algorithmic_bytes(B, K, SH2, D)
+    blend_gbps = per_kernel_bytes["blend_step"] / (blend_step_us * 1e-6) / 1e9
     flops, per_kernel_flops = algorithmic_flops(B, K, SH2, D)
     dom = max(names, key=lambda n: kern_us[n])
     hbm_us = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
@@ -395,6 +446,11 @@ def main():
         "kernel_us": {n: round(kern_us[n], 2) for n in names},
         "roofline": roof,
         # not part of the step: the optional input gradients, timed the same way
+        # not part of the step either: the blend path, fwd_blend + bwd_blend, cold rotation
+        "blend_step": {"us": round(blend_step_us, 2), "stability": BLEND_STABILITY,
+                       "temporal_weight": "U(0.5, 1.5)", "algorithmic_bytes": per_kernel_bytes["blend_step"],
+                       "achieved": round(blend_gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(blend_gbps / HBM_PEAK_GBS, 4)},
         "input_grads": {"kernel": "dinput_kernel", "us": round(kern_us["dinput_kernel"], 2), "bound": "hbm",
                         "achieved": round(per_kernel_bytes["dinput_kernel"] / (kern_us["dinput_kernel"] * 1e-6) / 1e9, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
