@@ -372,31 +372,32 @@ struct BwdCtx {
   bool rounds;  // K spans more than one round: apply S_r
 };
 
+// Every unit issues the same loads, from addresses chosen by select: a step
+// unit reads alpha'_t, beta'_t, S_r and four H rows; the readout reads x_K
+// (three times) and four h_s2 rows.  With no memory operation under a branch
+// the compiler's memory-counter waits stay exact, so the next unit's loads
+// (issued before this unit is consumed) stay in flight.
 __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx& c, int lane) {
   const int KU = c.K + 1;
   const int bi = u / KU;
   const int t = u - bi * KU;
   const int blk = c.blk0 + bi;
   const int sbase = blk * kBlock + 4 * c.kg;
-  const float* sv = c.saved + ((size_t)blk * c.NG + c.sg) * c.blk_stride;
-  if (t < c.K) {
-    U.al = ld4(sv + (size_t)(2 * t) * kPlane + 4 * lane);
-    U.be = ld4(sv + (size_t)(2 * t + 1) * kPlane + 4 * lane);
-    U.sr = c.rounds ? ld4(sv + (size_t)(2 * c.K + 1 + t / kChunk) * kPlane + 4 * lane) : v4f{1.f, 1.f, 1.f, 1.f};
+  const bool step = t < c.K;
+  const float* sv = c.saved + ((size_t)blk * c.NG + c.sg) * c.blk_stride + 4 * lane;
+  const int p0 = step ? 2 * t : 2 * c.K;
+  const int p1 = step ? 2 * t + 1 : 2 * c.K;
+  const int ps = (c.rounds && step) ? 2 * c.K + 1 + t / kChunk : 2 * c.K;  // a valid plane either way
+  U.al = ld4(sv + (size_t)p0 * kPlane);
+  U.be = ld4(sv + (size_t)p1 * kPlane);
+  U.sr = ld4(sv + (size_t)ps * kPlane);
+  const float* rows = step ? c.H + (size_t)t * c.SH2 : c.hs2;
+  const size_t rstride = step ? (size_t)c.K * c.SH2 : (size_t)c.SH2;  // floats between samples
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sc = min(sbase + i, c.B - 1);
-      U.h[i] = ld4_stream(c.H + ((size_t)sc * c.K + t) * c.SH2 + c.col);
-      U.dc[i] = c.dctx[(size_t)sc * c.D + c.state];
-    }
-  } else {
-    U.al = ld4(sv + (size_t)(2 * c.K) * kPlane + 4 * lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sc = min(sbase + i, c.B - 1);
-      U.h[i] = ld4_stream(c.hs2 + (size_t)sc * c.SH2 + c.col);
-      U.dc[i] = c.dctx[(size_t)sc * c.D + c.state];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int sc = min(sbase + i, c.B - 1);
+    U.h[i] = ld4_stream(rows + (size_t)sc * rstride + c.col);
+    U.dc[i] = c.dctx[(size_t)sc * c.D + c.state];
   }
 }
 
@@ -413,7 +414,7 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, int u, const BwdCt
     for (int i = 0; i < 4; ++i) {
       const int s = sbase + i;
       const bool ok = s < c.B;
-      const float dc = ok ? U.dc[i] * U.sr[i] : 0.f;
+      const float dc = ok ? (c.rounds ? U.dc[i] * U.sr[i] : U.dc[i]) : 0.f;
       const float da = dc * U.al[i];
       const float db = dc * U.be[i];
       const v4f h = ok ? U.h[i] : zero;
@@ -493,16 +494,18 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
     for (int pl = 0; pl < 3; ++pl) acc[q][pl] = v4f{0.f, 0.f, 0.f, 0.f};
 
   constexpr int S = kBwdWaves;
+  // Two-unit ring.  Requests are unconditional: past the last unit a wave
+  // re-loads the last unit (unused), so the compiler's waits stay exact.
   BwdUnit R0, R1;
   int u = wave;
-  if (u < n) bwd_load(R0, u, c, lane);
+  bwd_load(R0, min(u, n - 1), c, lane);
   while (u < n) {
-    if (u + S < n) bwd_load(R1, u + S, c, lane);
+    bwd_load(R1, min(u + S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
     bwd_compute(R0, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
     u += S;
     if (u >= n) break;
-    if (u + S < n) bwd_load(R0, u + S, c, lane);
+    bwd_load(R0, min(u + S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
     bwd_compute(R1, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
     u += S;
