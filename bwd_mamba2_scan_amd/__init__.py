@@ -6,6 +6,7 @@ is no CPU or PyTorch fallback: if the library is not built, every call raises.
 
 The entry points mirror include/mamba2_scan.h:
     fwd(h_history, h_s2, W_A, W_B, W_C)         -> (context, saved)
+        (h_history and h_s2 float32, or both bfloat16 for the *_bf16 entry points)
     bwd(h_history, h_s2, saved, d_context)      -> dict(dW_A, dW_B, dW_C[, d_a, d_b, d_c])
     bwd_partials(...), bwd_reduce(...)          -- the two phases of bwd
     bwd_input(W_A, W_B, W_C, saved, d_context, K) -> (d_h_history, d_h_s2)
@@ -54,6 +55,9 @@ _SIGNATURES = {
     "mamba2_scan_fwd_blend": (_c_int, [_c_int] * 4 + [_c_vp] * 10 + [_c_size, _c_vp]),
     "mamba2_scan_bwd_blend_workspace_bytes": (_c_size, [_c_int] * 4),
     "mamba2_scan_bwd_blend": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 8 + [_c_size, _c_vp]),
+    "mamba2_scan_fwd_bf16": (_c_int, [_c_int] * 4 + [_c_vp] * 7 + [_c_size, _c_vp]),
+    "mamba2_scan_bwd_bf16": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 8 + [_c_size, _c_vp]),
+    "mamba2_scan_bwd_partials_bf16": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 5 + [_c_size, _c_vp]),
     "mamba2_scan_strerror": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -105,16 +109,17 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _check(t, name, shape, device):
+def _check(t, name, shape, device, dtype=None):
     torch = _torch()
+    dtype = torch.float32 if dtype is None else dtype
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32 (got {t.dtype})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -131,6 +136,18 @@ def _stream(stream, device):
 def _dims(h_history, D):
     B, K, SH2 = (int(v) for v in h_history.shape)
     return B, K, SH2, int(D)
+
+
+def _trunk_dtype(h_history):
+    """float32, or bfloat16 for the reduced-precision trunk entry points."""
+    torch = _torch()
+    if h_history.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"h_history must be float32 or bfloat16 (got {h_history.dtype})")
+    return h_history.dtype
+
+
+def _is_bf16(dtype):
+    return dtype == _torch().bfloat16
 
 
 def _raise(status, where):
@@ -161,8 +178,9 @@ def fwd(h_history, h_s2, W_A, W_B, W_C, *, context=None, saved=None, stream=None
         raise ValueError("h_history must be [B, K, SH2] and W_A [SH2, D]")
     B, K, SH2, D = _dims(h_history, W_A.shape[1])
     dev = h_history.device
-    _check(h_history, "h_history", (B, K, SH2), None)
-    _check(h_s2, "h_s2", (B, SH2), dev)
+    tdt = _trunk_dtype(h_history)
+    _check(h_history, "h_history", (B, K, SH2), None, tdt)
+    _check(h_s2, "h_s2", (B, SH2), dev, tdt)
     for name, w in (("W_A", W_A), ("W_B", W_B), ("W_C", W_C)):
         _check(w, name, (SH2, D), dev)
     if context is None:
@@ -171,9 +189,11 @@ def fwd(h_history, h_s2, W_A, W_B, W_C, *, context=None, saved=None, stream=None
     if saved is None:
         saved = alloc_saved(B, K, SH2, D, dev)
     _check(saved, "saved", None, dev)
-    st = lib().mamba2_scan_fwd(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(W_A), _ptr(W_B), _ptr(W_C),
-                               _ptr(context), _ptr(saved), saved.numel() * 4, _stream(stream, dev))
-    _raise(st, "mamba2_scan_fwd")
+    fn, name = ((lib().mamba2_scan_fwd_bf16, "mamba2_scan_fwd_bf16") if _is_bf16(tdt)
+                else (lib().mamba2_scan_fwd, "mamba2_scan_fwd"))
+    st = fn(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(W_A), _ptr(W_B), _ptr(W_C),
+            _ptr(context), _ptr(saved), saved.numel() * 4, _stream(stream, dev))
+    _raise(st, name)
     return context, saved
 
 
@@ -182,8 +202,9 @@ def _bwd_args(h_history, h_s2, saved, d_context):
         raise ValueError("h_history must be [B, K, SH2] and d_context [B, D]")
     B, K, SH2, D = _dims(h_history, d_context.shape[1])
     dev = h_history.device
-    _check(h_history, "h_history", (B, K, SH2), None)
-    _check(h_s2, "h_s2", (B, SH2), dev)
+    tdt = _trunk_dtype(h_history)
+    _check(h_history, "h_history", (B, K, SH2), None, tdt)
+    _check(h_s2, "h_s2", (B, SH2), dev, tdt)
     _check(saved, "saved", None, dev)
     _check(d_context, "d_context", (B, D), dev)
     return B, K, SH2, D, dev
@@ -210,11 +231,13 @@ def bwd(h_history, h_s2, saved, d_context, *, workspace=None, out=None, debug=Fa
     for n in ("dW_A", "dW_B", "dW_C"):
         _check(out[n], n, (SH2, D), dev)
     d_a, d_b, d_c = _debug_bufs(debug, B, K, D, dev)
-    st = lib().mamba2_scan_bwd(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(saved), saved.numel() * 4,
-                               _ptr(d_context), _ptr(out["dW_A"]), _ptr(out["dW_B"]), _ptr(out["dW_C"]),
-                               _ptr(d_a), _ptr(d_b), _ptr(d_c), _ptr(workspace), workspace.numel() * 4,
-                               _stream(stream, dev))
-    _raise(st, "mamba2_scan_bwd")
+    fn, name = ((lib().mamba2_scan_bwd_bf16, "mamba2_scan_bwd_bf16") if _is_bf16(h_history.dtype)
+                else (lib().mamba2_scan_bwd, "mamba2_scan_bwd"))
+    st = fn(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(saved), saved.numel() * 4,
+            _ptr(d_context), _ptr(out["dW_A"]), _ptr(out["dW_B"]), _ptr(out["dW_C"]),
+            _ptr(d_a), _ptr(d_b), _ptr(d_c), _ptr(workspace), workspace.numel() * 4,
+            _stream(stream, dev))
+    _raise(st, name)
     res = dict(out)
     if debug:
         res.update(d_a=d_a, d_b=d_b, d_c=d_c)
@@ -226,10 +249,11 @@ def bwd_partials(h_history, h_s2, saved, d_context, workspace, *, debug=False, s
     B, K, SH2, D, dev = _bwd_args(h_history, h_s2, saved, d_context)
     _check(workspace, "workspace", None, dev)
     d_a, d_b, d_c = _debug_bufs(debug, B, K, D, dev)
-    st = lib().mamba2_scan_bwd_partials(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(saved),
-                                        saved.numel() * 4, _ptr(d_context), _ptr(d_a), _ptr(d_b), _ptr(d_c),
-                                        _ptr(workspace), workspace.numel() * 4, _stream(stream, dev))
-    _raise(st, "mamba2_scan_bwd_partials")
+    fn, name = ((lib().mamba2_scan_bwd_partials_bf16, "mamba2_scan_bwd_partials_bf16") if _is_bf16(h_history.dtype)
+                else (lib().mamba2_scan_bwd_partials, "mamba2_scan_bwd_partials"))
+    st = fn(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(saved), saved.numel() * 4, _ptr(d_context),
+            _ptr(d_a), _ptr(d_b), _ptr(d_c), _ptr(workspace), workspace.numel() * 4, _stream(stream, dev))
+    _raise(st, name)
     return dict(d_a=d_a, d_b=d_b, d_c=d_c) if debug else {}
 
 

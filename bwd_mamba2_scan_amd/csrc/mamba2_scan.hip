@@ -79,6 +79,28 @@ __device__ __forceinline__ v4f ld4_stream(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
 }
 __device__ __forceinline__ void st_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
+// Trunk inputs (h_history, h_s2) come as fp32 or as bf16 bit patterns; either
+// way four consecutive elements arrive as one streamed load and widen to fp32
+// exactly (a bf16 value is the top half of the fp32 with the same value).
+typedef unsigned short bf16_t;
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+template <class T>
+__device__ __forceinline__ v4f ld4_in(const T* p);
+template <>
+__device__ __forceinline__ v4f ld4_in<float>(const float* p) {
+  return ld4_stream(p);
+}
+template <>
+__device__ __forceinline__ v4f ld4_in<bf16_t>(const bf16_t* p) {
+  const v2u w = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+  v4f r;
+  r[0] = __uint_as_float(w[0] << 16);
+  r[1] = __uint_as_float(w[0] & 0xffff0000u);
+  r[2] = __uint_as_float(w[1] << 16);
+  r[3] = __uint_as_float(w[1] & 0xffff0000u);
+  return r;
+}
 __device__ __forceinline__ void st4_stream(float* p, v4f v) {
   __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
 }
@@ -107,10 +129,10 @@ __host__ __device__ __forceinline__ int saved_planes(int K) {
 // min(kFwdPrefetch, SH2/16) history loads in flight: enough in total to
 // saturate HBM without queueing so deep that the first data arrives late.
 // The first loads of round r+1 go out before the scan of round r.
-template <int NKC>  // SH2 / 16 trunk chunks
+template <int NKC, class T>  // SH2 / 16 trunk chunks; T = fp32 or bf16 trunk inputs
 __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     int B, int K, int NG, int NB,
-    const float* __restrict__ H, const float* __restrict__ hs2,
+    const T* __restrict__ H, const T* __restrict__ hs2,
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
     const float* __restrict__ stab, float* __restrict__ ctx, float* __restrict__ saved) {
   constexpr int SH2 = NKC * 16;
@@ -174,18 +196,18 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   // gradient).  Readout chunks kc = wave + 8r, then this wave's first step:
   // all issued now, consumed by the MFMAs below as they land.
   const int smp_a = min(blk * kBlock + m, B - 1);
-  const float* crow = hs2 + (size_t)smp_a * SH2 + 4 * kg;
+  const T* crow = hs2 + (size_t)smp_a * SH2 + 4 * kg;
   v4f hc[NCR];
 #pragma unroll
   for (int r = 0; r < NCR; ++r) {
     const int kc = wave + kFwdWaves * r;
-    if (kc < NKC) hc[r] = ld4_stream(crow + kc * 16);
+    if (kc < NKC) hc[r] = ld4_in(crow + kc * 16);
   }
-  const float* hbase = H + (size_t)smp_a * K * SH2 + 4 * kg;
+  const T* hbase = H + (size_t)smp_a * K * SH2 + 4 * kg;
   v4f hv[NKC];
   if (wave < K) {
 #pragma unroll
-    for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4_stream(hbase + (size_t)wave * SH2 + kc * 16);
+    for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4_in(hbase + (size_t)wave * SH2 + kc * 16);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -239,13 +261,13 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
           accb = mfma16x16x4(hv[kc][i], wb[i], accb);
         }
         // keep PF loads of this step in flight
-        if (kc + PF < NKC) hv[kc + PF] = ld4_stream(hbase + (size_t)t * SH2 + (kc + PF) * 16);
+        if (kc + PF < NKC) hv[kc + PF] = ld4_in(hbase + (size_t)t * SH2 + (kc + PF) * 16);
         __builtin_amdgcn_sched_barrier(0);
       }
       // next round's first loads go out before this round's exchange and scan
       if (t + kChunk < K) {
 #pragma unroll
-        for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4_stream(hbase + (size_t)(t + kChunk) * SH2 + kc * 16);
+        for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4_in(hbase + (size_t)(t + kChunk) * SH2 + kc * 16);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -362,10 +384,11 @@ struct BwdUnit {
   float dc[4];  // d_context of samples 4kg+i, state n (unmasked)
 };
 
+template <class T>
 struct BwdCtx {
   int B, K, SH2, D, NG, sg, blk0, col, state, kg;
-  const float* H;
-  const float* hs2;
+  const T* H;
+  const T* hs2;
   const float* saved;
   const float* dctx;
   size_t blk_stride;
@@ -377,7 +400,8 @@ struct BwdCtx {
 // (three times) and four h_s2 rows.  With no memory operation under a branch
 // the compiler's memory-counter waits stay exact, so the next unit's loads
 // (issued before this unit is consumed) stay in flight.
-__device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx& c, int lane) {
+template <class T>
+__device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, int lane) {
   const int KU = c.K + 1;
   const int bi = u / KU;
   const int t = u - bi * KU;
@@ -391,17 +415,18 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx& c, int
   U.al = ld4(sv + (size_t)p0 * kPlane);
   U.be = ld4(sv + (size_t)p1 * kPlane);
   U.sr = ld4(sv + (size_t)ps * kPlane);
-  const float* rows = step ? c.H + (size_t)t * c.SH2 : c.hs2;
+  const T* rows = step ? c.H + (size_t)t * c.SH2 : c.hs2;
   const size_t rstride = step ? (size_t)c.K * c.SH2 : (size_t)c.SH2;  // floats between samples
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sc = min(sbase + i, c.B - 1);
-    U.h[i] = ld4_stream(rows + (size_t)sc * rstride + c.col);
+    U.h[i] = ld4_in(rows + (size_t)sc * rstride + c.col);
     U.dc[i] = c.dctx[(size_t)sc * c.D + c.state];
   }
 }
 
-__device__ __forceinline__ void bwd_compute(const BwdUnit& U, int u, const BwdCtx& c, v4f (&acc)[4][3],
+template <class Ctx>
+__device__ __forceinline__ void bwd_compute(const BwdUnit& U, int u, const Ctx& c, v4f (&acc)[4][3],
                                             float* __restrict__ d_a_out, float* __restrict__ d_b_out,
                                             float* __restrict__ d_c_out, bool write_dbg) {
   const int KU = c.K + 1;
@@ -442,9 +467,10 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, int u, const BwdCt
   }
 }
 
+template <class T>
 __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
     int B, int K, int SH2, int NG, int NB, int P, int BPW,
-    const float* __restrict__ H, const float* __restrict__ hs2,
+    const T* __restrict__ H, const T* __restrict__ hs2,
     const float* __restrict__ saved, const float* __restrict__ dctx,
     float* __restrict__ d_a_out, float* __restrict__ d_b_out, float* __restrict__ d_c_out,
     float* __restrict__ ws) {
@@ -467,7 +493,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   const int m = lane & 15;
   const bool write_dbg = (jb == 0);
 
-  BwdCtx c;
+  BwdCtx<T> c;
   c.B = B;
   c.K = K;
   c.SH2 = SH2;
@@ -1013,15 +1039,15 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? MAMBA2_SCAN_OK : MAMBA2_SCAN_EHIP;
 }
 
-template <int NKC>
-void launch_fwd(const Plan& pl, const float* H, const float* hs2, const float* WA, const float* WB,
+template <int NKC, class T>
+void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const float* WB,
                 const float* WC, const float* stab, float* ctx, float* saved, hipStream_t st) {
   const int grid = 8 * pl.NG * ((pl.NB + 7) / 8);
-  hipLaunchKernelGGL(fwd_kernel<NKC>, dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
+  hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
                      hs2, WA, WB, WC, stab, ctx, saved);
 }
 
-int check_bwd_common(const Plan& pl, const float* H, const float* hs2, const void* saved, size_t saved_bytes,
+int check_bwd_common(const Plan& pl, const void* H, const void* hs2, const void* saved, size_t saved_bytes,
                      const float* dctx, const float* da, const float* db, const float* dc, const void* ws,
                      size_t ws_bytes) {
   if (!H || !hs2 || !saved || !dctx || !ws) return MAMBA2_SCAN_ENULL;
@@ -1040,10 +1066,11 @@ int check_reduce(const Plan& pl, const void* ws, size_t ws_bytes, const float* d
   return MAMBA2_SCAN_OK;
 }
 
-void launch_partials(const Plan& pl, const float* H, const float* hs2, const void* saved, const float* dctx,
+template <class T>
+void launch_partials(const Plan& pl, const T* H, const T* hs2, const void* saved, const float* dctx,
                      float* da, float* db, float* dc, void* ws, hipStream_t st) {
   const int grid = 8 * pl.V * ((pl.P + 7) / 8);
-  hipLaunchKernelGGL(bwd_partials_kernel, dim3(grid), dim3(kBwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
+  hipLaunchKernelGGL(bwd_partials_kernel<T>, dim3(grid), dim3(kBwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
                      pl.NB, pl.P, pl.BPW, H, hs2, static_cast<const float*>(saved), dctx, da, db, dc,
                      static_cast<float*>(ws));
 }
@@ -1057,7 +1084,7 @@ void launch_reduce(const Plan& pl, const void* ws, float* dWA, float* dWB, float
                      static_cast<const float*>(ws), dWA, dWB, dWC, Pw, wsw, dw);
 }
 
-int check_fwd(const Plan& pl, const float* H, const float* hs2, const float* WA, const float* WB, const float* WC,
+int check_fwd(const Plan& pl, const void* H, const void* hs2, const float* WA, const float* WB, const float* WC,
               const float* ctx, const void* saved, size_t saved_bytes) {
   if (!H || !hs2 || !WA || !WB || !WC || !ctx || !saved) return MAMBA2_SCAN_ENULL;
   if (saved_bytes < pl.saved_bytes) return MAMBA2_SCAN_ESIZE;
@@ -1067,18 +1094,19 @@ int check_fwd(const Plan& pl, const float* H, const float* hs2, const float* WA,
   return MAMBA2_SCAN_OK;
 }
 
-int run_fwd(const Plan& pl, const float* H, const float* hs2, const float* WA, const float* WB, const float* WC,
+template <class T>
+int run_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const float* WB, const float* WC,
             const float* stab, float* ctx, void* saved, hipStream_t s) {
   float* sv = static_cast<float*>(saved);
   switch (pl.SH2 / 64) {
-    case 1: launch_fwd<4>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 2: launch_fwd<8>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 3: launch_fwd<12>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 4: launch_fwd<16>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 5: launch_fwd<20>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 6: launch_fwd<24>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 7: launch_fwd<28>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 8: launch_fwd<32>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 1: launch_fwd<4, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 2: launch_fwd<8, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 3: launch_fwd<12, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 4: launch_fwd<16, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 5: launch_fwd<20, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 6: launch_fwd<24, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 7: launch_fwd<28, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 8: launch_fwd<32, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
     default: return MAMBA2_SCAN_EUNSUPPORTED;
   }
   return launch_status();
@@ -1206,6 +1234,53 @@ int mamba2_scan_bwd(int B, int K, int SH2, int STATE_D, const float* h_history, 
   if (st != MAMBA2_SCAN_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   launch_partials(pl, h_history, h_s2, saved, d_context, d_a, d_b, d_c, workspace, s);
+  st = launch_status();
+  if (st != MAMBA2_SCAN_OK) return st;
+  launch_reduce(pl, workspace, dW_A, dW_B, dW_C, s);
+  return launch_status();
+}
+
+int mamba2_scan_fwd_bf16(int B, int K, int SH2, int STATE_D, const void* h_history, const void* h_s2,
+                         const float* W_A, const float* W_B, const float* W_C, float* context, void* saved,
+                         size_t saved_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_fwd(pl, h_history, h_s2, W_A, W_B, W_C, context, saved, saved_bytes);
+  if (st != MAMBA2_SCAN_OK) return st;
+  return run_fwd(pl, static_cast<const bf16_t*>(h_history), static_cast<const bf16_t*>(h_s2), W_A, W_B, W_C,
+                 nullptr, context, saved, static_cast<hipStream_t>(stream));
+}
+
+int mamba2_scan_bwd_partials_bf16(int B, int K, int SH2, int STATE_D, const void* h_history, const void* h_s2,
+                                  const void* saved, size_t saved_bytes, const float* d_context, float* d_a,
+                                  float* d_b, float* d_c, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_bwd_common(pl, h_history, h_s2, saved, saved_bytes, d_context, d_a, d_b, d_c, workspace,
+                        workspace_bytes);
+  if (st != MAMBA2_SCAN_OK) return st;
+  launch_partials(pl, static_cast<const bf16_t*>(h_history), static_cast<const bf16_t*>(h_s2), saved, d_context,
+                  d_a, d_b, d_c, workspace, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int mamba2_scan_bwd_bf16(int B, int K, int SH2, int STATE_D, const void* h_history, const void* h_s2,
+                         const void* saved, size_t saved_bytes, const float* d_context, float* dW_A, float* dW_B,
+                         float* dW_C, float* d_a, float* d_b, float* d_c, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_bwd_common(pl, h_history, h_s2, saved, saved_bytes, d_context, d_a, d_b, d_c, workspace,
+                        workspace_bytes);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_reduce(pl, workspace, workspace_bytes, dW_A, dW_B, dW_C);
+  if (st != MAMBA2_SCAN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_partials(pl, static_cast<const bf16_t*>(h_history), static_cast<const bf16_t*>(h_s2), saved, d_context,
+                  d_a, d_b, d_c, workspace, s);
   st = launch_status();
   if (st != MAMBA2_SCAN_OK) return st;
   launch_reduce(pl, workspace, dW_A, dW_B, dW_C, s);

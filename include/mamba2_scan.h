@@ -203,6 +203,37 @@ int mamba2_scan_bwd_blend(int B, int K, int SH2, int STATE_D,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * Reduced-precision trunk inputs: h_history and h_s2 hold bfloat16 values
+ * (their 16-bit patterns, the top half of the fp32 with the same value),
+ * halving the bytes of the dominant reads.  Every other argument, the
+ * arithmetic (fp32, widening each input exactly) and the results are as for
+ * the fp32 entry point of the same name: mamba2_scan_fwd,
+ * mamba2_scan_bwd_partials and mamba2_scan_bwd.  The same `saved`,
+ * workspace and second phase (mamba2_scan_bwd_reduce) serve both.
+ * h_history and h_s2 must be 16-byte aligned.
+ */
+int mamba2_scan_fwd_bf16(int B, int K, int SH2, int STATE_D,
+                         const void* h_history, const void* h_s2,
+                         const float* W_A, const float* W_B, const float* W_C,
+                         float* context, void* saved, size_t saved_bytes,
+                         void* stream);
+int mamba2_scan_bwd_partials_bf16(int B, int K, int SH2, int STATE_D,
+                                  const void* h_history, const void* h_s2,
+                                  const void* saved, size_t saved_bytes,
+                                  const float* d_context,
+                                  float* d_a, float* d_b, float* d_c,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+int mamba2_scan_bwd_bf16(int B, int K, int SH2, int STATE_D,
+                         const void* h_history, const void* h_s2,
+                         const void* saved, size_t saved_bytes,
+                         const float* d_context,
+                         float* dW_A, float* dW_B, float* dW_C,
+                         float* d_a, float* d_b, float* d_c,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Static text for a status code. */
 const char* mamba2_scan_strerror(int status);
 

@@ -87,3 +87,16 @@ def blend_extras(B: int, SH2: int, seed: int):
         "d_h_enriched": rng.standard_normal((B, SH2), dtype=np.float32),
         "temporal_weight": rng.uniform(0.5, 1.5, SH2).astype(np.float32),
     }
+
+
+def bf16_round(x):
+    """Round float32 values to bfloat16 (nearest, ties to even).
+
+    Returns (bits, values): the 16-bit patterns (uint16) the reduced-precision
+    entry points take, and the same values widened back to float32 for the
+    oracle and the fp32 entry points.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    values = (bits.astype(np.uint32) << 16).view(np.float32)
+    return bits, values

@@ -23,6 +23,7 @@ def test_exports_every_header_symbol(L):
         "mamba2_scan_saved_bytes", "mamba2_scan_bwd_workspace_bytes", "mamba2_scan_fwd",
         "mamba2_scan_bwd", "mamba2_scan_bwd_partials", "mamba2_scan_bwd_reduce", "mamba2_scan_bwd_input",
         "mamba2_scan_fwd_blend", "mamba2_scan_bwd_blend_workspace_bytes", "mamba2_scan_bwd_blend",
+        "mamba2_scan_fwd_bf16", "mamba2_scan_bwd_bf16", "mamba2_scan_bwd_partials_bf16",
         "mamba2_scan_strerror",
     }
     for n in names:
@@ -75,6 +76,11 @@ def test_bad_dims(L, dims, code):
     assert L.mamba2_scan_bwd_reduce(*dims, fake, 1 << 40, fake, fake, fake, None) == code
     assert L.mamba2_scan_bwd_input(*dims, fake, fake, fake, fake, 1 << 40, fake, fake, fake, None) == code
     assert m2.blend_workspace_bytes(*dims) == 0
+    assert L.mamba2_scan_fwd_bf16(*dims, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None) == code
+    assert L.mamba2_scan_bwd_bf16(*dims, fake, fake, fake, 1 << 40, fake, fake, fake, fake, None, None, None,
+                                  fake, 1 << 40, None) == code
+    assert L.mamba2_scan_bwd_partials_bf16(*dims, fake, fake, fake, 1 << 40, fake, None, None, None,
+                                           fake, 1 << 40, None) == code
     assert L.mamba2_scan_fwd_blend(*dims, fake, fake, fake, fake, fake, None, None, fake, fake, fake, 1 << 40,
                                    None) == code
     assert L.mamba2_scan_bwd_blend(*dims, fake, fake, fake, 1 << 40, None, fake, fake, fake, fake, fake, None,
@@ -185,3 +191,18 @@ def test_bwd_blend_argument_checks(L):
     assert call(wsb=m2.workspace_bytes(*dims)) == m2.ESIZE
     for kw, off in (("dhe", 4), ("w", 8), ("dw", 2), ("wk", 4)):
         assert call(**{kw: ctypes.c_void_p(0x50000 + off)}) == m2.EALIGN, kw
+
+
+def test_bf16_entry_points_check_like_fp32(L):
+    # same checks as the fp32 entry points: one defect per call, nothing launched
+    dims = (64, 8, 256, 16)
+    sv = m2.saved_bytes(*dims)
+    ws = m2.workspace_bytes(*dims)
+    g = ctypes.c_void_p(0x60000)
+    assert L.mamba2_scan_fwd_bf16(*dims, None, g, g, g, g, g, g, sv, None) == m2.ENULL
+    assert L.mamba2_scan_fwd_bf16(*dims, g, g, g, g, g, g, g, sv - 4, None) == m2.ESIZE
+    assert L.mamba2_scan_fwd_bf16(*dims, ctypes.c_void_p(0x60008), g, g, g, g, g, g, sv, None) == m2.EALIGN
+    assert L.mamba2_scan_bwd_bf16(*dims, g, None, g, sv, g, g, g, g, None, None, None, g, ws, None) == m2.ENULL
+    assert L.mamba2_scan_bwd_bf16(*dims, g, g, g, sv, g, g, g, g, None, None, None, g, ws - 4, None) == m2.ESIZE
+    assert L.mamba2_scan_bwd_partials_bf16(*dims, g, ctypes.c_void_p(0x60002), g, sv, g, None, None, None, g, ws,
+                                           None) == m2.EALIGN
