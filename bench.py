@@ -379,6 +379,50 @@ def main():
     blend_step_us = e0.elapsed_time(e1) * 1e3 / (reps * R)
     del bg
 
+    # ---- bf16 trunk inputs (the *_bf16 entry points), same cold rotation
+    for st_ in sets:
+        st_["h16"] = st_["h_history"].to(torch.bfloat16)
+        st_["hs16"] = st_["h_s2"].to(torch.bfloat16)
+
+    def fwd16(s):
+        m2.fwd(s["h16"], s["hs16"], s["W_A"], s["W_B"], s["W_C"], context=s["context"], saved=s["saved"])
+
+    def partials16(s):
+        m2.bwd_partials(s["h16"], s["hs16"], s["saved"], s["d_context"], s["ws"])
+
+    def step16(i):
+        fwd16(sets[i % R])
+        sb = sets[(i - R // 2) % R]
+        partials16(sb)
+        reduce(sb)
+
+    def graph_us(fn_step, count):
+        with torch.cuda.stream(stream):
+            for i in range(count):
+                fn_step(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(count):
+                    fn_step(i)
+            torch.cuda.synchronize()
+            g.replay()
+            reps = max(2, args.steps // count)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * count)
+
+    bf16_step_us = graph_us(step16, R)
+    bf16_kern_us = {"fwd_kernel": graph_us(lambda i: fwd16(sets[i % R]), 8 * R),
+                    "bwd_partials_kernel": graph_us(lambda i: partials16(sets[i % R]), 8 * R)}
+    for st_ in sets:
+        del st_["h16"], st_["hs16"]
+
     # ---- copy ceiling: a 1 GiB device-to-device copy (read + write bytes)
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -398,6 +442,9 @@ def main():
 
     step_bytes, per_kernel_bytes = algorithmic_bytes(B, K, SH2, D)
     blend_gbps = per_kernel_bytes["blend_step"] / (blend_step_us * 1e-6) / 1e9
+    # bf16 trunk inputs: h_history and h_s2 move half the bytes, twice per step
+    bf16_bytes = step_bytes - (B * K * SH2 + B * SH2) * 4
+    bf16_gbps = bf16_bytes / (bf16_step_us * 1e-6) / 1e9
     flops, per_kernel_flops = algorithmic_flops(B, K, SH2, D)
     dom = max(names, key=lambda n: kern_us[n])
     hbm_us = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
@@ -446,6 +493,11 @@ def main():
         "kernel_us": {n: round(kern_us[n], 2) for n in names},
         "roofline": roof,
         # not part of the step: the optional input gradients, timed the same way
+        # the same step with bf16 h_history and h_s2 (fp32 arithmetic): not the headline
+        "bf16_step": {"us": round(bf16_step_us, 2), "algorithmic_bytes": bf16_bytes,
+                      "achieved": round(bf16_gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(bf16_gbps / HBM_PEAK_GBS, 4),
+                      "kernel_us": {k: round(v, 2) for k, v in bf16_kern_us.items()}},
         # not part of the step either: the blend path, fwd_blend + bwd_blend, cold rotation
         "blend_step": {"us": round(blend_step_us, 2), "stability": BLEND_STABILITY,
                        "temporal_weight": "U(0.5, 1.5)", "algorithmic_bytes": per_kernel_bytes["blend_step"],

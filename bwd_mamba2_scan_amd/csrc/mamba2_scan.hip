@@ -91,6 +91,20 @@ template <>
 __device__ __forceinline__ v4f ld4_in<float>(const float* p) {
   return ld4_stream(p);
 }
+// Eight consecutive bf16 values as one 16-byte streamed load, widened into
+// two groups of four.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void ld8_bf16(const bf16_t* p, v4f& lo, v4f& hi) {
+  const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  lo[0] = __uint_as_float(w[0] << 16);
+  lo[1] = __uint_as_float(w[0] & 0xffff0000u);
+  lo[2] = __uint_as_float(w[1] << 16);
+  lo[3] = __uint_as_float(w[1] & 0xffff0000u);
+  hi[0] = __uint_as_float(w[2] << 16);
+  hi[1] = __uint_as_float(w[2] & 0xffff0000u);
+  hi[2] = __uint_as_float(w[3] << 16);
+  hi[3] = __uint_as_float(w[3] & 0xffff0000u);
+}
 template <>
 __device__ __forceinline__ v4f ld4_in<bf16_t>(const bf16_t* p) {
   const v2u w = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
@@ -137,7 +151,16 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     const float* __restrict__ stab, float* __restrict__ ctx, float* __restrict__ saved) {
   constexpr int SH2 = NKC * 16;
   constexpr int NCR = (NKC + kFwdWaves - 1) / kFwdWaves;                   // readout chunks per wave
-  constexpr int PF = kFwdPrefetch < NKC ? kFwdPrefetch : NKC;              // history loads in flight
+  constexpr int NCRP = (NKC / 2 + kFwdWaves - 1) / kFwdWaves;              // readout pairs per wave (bf16)
+  // bf16 inputs load in pairs of chunks: lane (kg, m) takes features
+  // 32p + 8kg .. +7 of pair p, the first four for chunk 2p, the rest for
+  // chunk 2p+1 (the weight slab is staged in the same order).
+  constexpr bool PAIR = sizeof(T) == 2;
+#ifndef FWD_PAIR_PF
+#define FWD_PAIR_PF 3
+#endif
+  constexpr int PFP = PAIR ? (FWD_PAIR_PF < NKC / 2 ? FWD_PAIR_PF : NKC / 2) : 0;  // pairs in flight
+  constexpr int PF = PAIR ? 2 * PFP : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC);   // chunks in flight
   __shared__ v4f sWa[NKC * 64];
   __shared__ v4f sWb[NKC * 64];
   __shared__ v4f sWc[NKC * 64];
@@ -183,7 +206,10 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
         const int mat = f / NW4, r = f - mat * NW4;
         const int j = r >> 2, s4 = r & 3;
         float* dst = reinterpret_cast<float*>(mat == 0 ? sWa : (mat == 1 ? sWb : sWc));
-        const int base = ((j >> 4) * 64 + 16 * ((j >> 2) & 3) + 4 * s4) * 4 + (j & 3);
+        // feature j -> (chunk, k-group, element) of the A/B operand order
+        const int jc = PAIR ? 2 * (j >> 5) + ((j & 7) >> 2) : (j >> 4);
+        const int jg = PAIR ? ((j & 31) >> 3) : ((j >> 2) & 3);
+        const int base = (jc * 64 + 16 * jg + 4 * s4) * 4 + (j & 3);
 #pragma unroll
         for (int q = 0; q < 4; ++q) dst[base + 4 * q] = wr[it][q];
       }
@@ -196,33 +222,64 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   // gradient).  Readout chunks kc = wave + 8r, then this wave's first step:
   // all issued now, consumed by the MFMAs below as they land.
   const int smp_a = min(blk * kBlock + m, B - 1);
-  const T* crow = hs2 + (size_t)smp_a * SH2 + 4 * kg;
-  v4f hc[NCR];
+  const int koff = PAIR ? 8 * kg : 4 * kg;
+  const T* crow = hs2 + (size_t)smp_a * SH2 + koff;
+  v4f hc[PAIR ? 2 * NCRP : NCR];
+  if constexpr (PAIR) {
 #pragma unroll
-  for (int r = 0; r < NCR; ++r) {
-    const int kc = wave + kFwdWaves * r;
-    if (kc < NKC) hc[r] = ld4_in(crow + kc * 16);
+    for (int r = 0; r < NCRP; ++r) {
+      const int pc = wave + kFwdWaves * r;
+      if (pc < NKC / 2) ld8_bf16(crow + pc * 32, hc[2 * r], hc[2 * r + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NCR; ++r) {
+      const int kc = wave + kFwdWaves * r;
+      if (kc < NKC) hc[r] = ld4_in(crow + kc * 16);
+    }
   }
-  const T* hbase = H + (size_t)smp_a * K * SH2 + 4 * kg;
+  const T* hbase = H + (size_t)smp_a * K * SH2 + koff;
   v4f hv[NKC];
+  // chunk kc (or pair kc/2) of history step t into hv
+  auto load_chunk = [&](int t, int kc) {
+    if constexpr (PAIR)
+      ld8_bf16(hbase + (size_t)t * SH2 + (kc >> 1) * 32, hv[kc], hv[kc + 1]);
+    else
+      hv[kc] = ld4_in(hbase + (size_t)t * SH2 + kc * 16);
+  };
   if (wave < K) {
 #pragma unroll
-    for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4_in(hbase + (size_t)wave * SH2 + kc * 16);
+    for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(wave, kc);
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // (3) readout partial over this wave's chunks
   {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (PAIR) {
 #pragma unroll
-    for (int r = 0; r < NCR; ++r) {
-      const int kc = wave + kFwdWaves * r;
-      if (kc < NKC) {
-        const v4f bv = sWc[kc * 64 + lane];
-        acc = mfma16x16x4(hc[r][0], bv[0], acc);
-        acc = mfma16x16x4(hc[r][1], bv[1], acc);
-        acc = mfma16x16x4(hc[r][2], bv[2], acc);
-        acc = mfma16x16x4(hc[r][3], bv[3], acc);
+      for (int r = 0; r < NCRP; ++r) {
+        const int pc = wave + kFwdWaves * r;
+        if (pc < NKC / 2) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const v4f bv = sWc[(2 * pc + h) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = mfma16x16x4(hc[2 * r + h][i], bv[i], acc);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < NCR; ++r) {
+        const int kc = wave + kFwdWaves * r;
+        if (kc < NKC) {
+          const v4f bv = sWc[kc * 64 + lane];
+          acc = mfma16x16x4(hc[r][0], bv[0], acc);
+          acc = mfma16x16x4(hc[r][1], bv[1], acc);
+          acc = mfma16x16x4(hc[r][2], bv[2], acc);
+          acc = mfma16x16x4(hc[r][3], bv[3], acc);
+        }
       }
     }
 #pragma unroll
@@ -260,14 +317,18 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
           acca = mfma16x16x4(hv[kc][i], wa[i], acca);
           accb = mfma16x16x4(hv[kc][i], wb[i], accb);
         }
-        // keep PF loads of this step in flight
-        if (kc + PF < NKC) hv[kc + PF] = ld4_in(hbase + (size_t)t * SH2 + (kc + PF) * 16);
+        // keep PF chunks of this step in flight (pairs: after a pair's second chunk)
+        if constexpr (PAIR) {
+          if ((kc & 1) && kc + 1 + PF - 2 < NKC - 1 && kc + PF < NKC) load_chunk(t, kc + PF - 1);
+        } else {
+          if (kc + PF < NKC) load_chunk(t, kc + PF);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       // next round's first loads go out before this round's exchange and scan
       if (t + kChunk < K) {
 #pragma unroll
-        for (int kc = 0; kc < PF; ++kc) hv[kc] = ld4_in(hbase + (size_t)(t + kChunk) * SH2 + kc * 16);
+        for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(t + kChunk, kc);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

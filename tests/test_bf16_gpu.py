@@ -1,9 +1,11 @@
 """The bfloat16 trunk-input entry points (h_history, h_s2 as bf16) on an MI355X.
 
 The oracle runs on the same bf16-rounded values, so the tolerances are the
-fp32 path's.  And since each bf16 value widens to fp32 exactly, the bf16
-entry points must give bit-identical results to the fp32 entry points fed
-the widened values.
+fp32 path's.  Each bf16 value widens to fp32 exactly; the forward then sums
+the features in another order (a lane loads eight bf16 features at once), so
+against the fp32 entry points fed the widened values the results agree to
+fp32 rounding (checked at 1e-5), and the backward, whose order is the same,
+bit for bit.
 """
 from __future__ import annotations
 
@@ -52,11 +54,17 @@ def check(inputs, debug=True):
     if debug:
         for name in ("d_a", "d_b", "d_c"):
             assert_elementwise(g[name].cpu().numpy(), getattr(b, name), name)
-    # the same values through the fp32 entry points: the same bits
+    # the same values through the fp32 entry points
     ctx32, saved32, g32 = run(t32, debug)
-    assert torch.equal(ctx, ctx32) and torch.equal(saved, saved32)
-    for name in g:
-        assert torch.equal(g[name], g32[name]), name
+    assert_elementwise(ctx.cpu().numpy(), ctx32.cpu().numpy().astype(np.float64), "context vs fp32 path", tol=1e-5)
+    for name in ("dW_A", "dW_B", "dW_C"):
+        assert_l1(g[name].cpu().numpy(), g32[name].cpu().numpy().astype(np.float64), name + " vs fp32 path", tol=1e-5)
+    # the backward alone, on one forward's saved terms: the same bits
+    g16b = m2.bwd(t16["h_history"], t16["h_s2"], saved32, t16["d_context"])
+    g32b = m2.bwd(t32["h_history"], t32["h_s2"], saved32, t32["d_context"])
+    torch.cuda.synchronize()
+    for name in ("dW_A", "dW_B", "dW_C"):
+        assert torch.equal(g16b[name], g32b[name]), name
 
 
 @pytest.mark.parametrize("B,K,SH2,D", EDGE_SHAPES, ids=lambda v: str(v))
