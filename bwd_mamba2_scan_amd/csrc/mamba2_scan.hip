@@ -59,6 +59,7 @@ constexpr int kFwdWaves = 8;
 constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
 constexpr int kFwdPrefetch = 6;    // history loads each forward wave keeps in flight
 constexpr int kRegRounds = 8;      // rounds whose gate product the forward keeps in registers
+constexpr int kFwdChunkTarget = 512;  // forward work-groups a chunked history aims for
 constexpr int kBwdWaves = 8;
 constexpr int kBwdTargetGroups = 256;  // backward work-groups to aim for (one per CU)
 constexpr int kRedThreads = 256;
@@ -148,7 +149,8 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     int B, int K, int NG, int NB,
     const T* __restrict__ H, const T* __restrict__ hs2,
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
-    const float* __restrict__ stab, float* __restrict__ ctx, float* __restrict__ saved) {
+    const float* __restrict__ stab, float* __restrict__ ctx, float* __restrict__ saved,
+    int L, int C, int mode) {
   constexpr int SH2 = NKC * 16;
   constexpr int NCR = (NKC + kFwdWaves - 1) / kFwdWaves;                   // readout chunks per wave
   constexpr int NCRP = (NKC / 2 + kFwdWaves - 1) / kFwdWaves;              // readout pairs per wave (bf16)
@@ -172,8 +174,14 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   const int xcd = blockIdx.x & 7;
   const int round = blockIdx.x >> 3;
   const int sg = round % NG;
-  const int blk = (round / NG) * 8 + xcd;
+  const int cidx = (round / NG) % C;  // history chunk of this work-group (C = 1: the whole history)
+  const int blk = (round / NG / C) * 8 + xcd;
   if (blk >= NB) return;
+  // steps [t0, t1) of this chunk: rounds r0 .. r1-1 (a round is kChunk steps)
+  const int t0 = cidx * L;
+  const int t1 = cidx == C - 1 ? K : t0 + L;
+  const int r0 = t0 / kChunk;
+  const int r1 = (t1 + kChunk - 1) / kChunk;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -247,9 +255,9 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     else
       hv[kc] = ld4_in(hbase + (size_t)t * SH2 + kc * 16);
   };
-  if (wave < K) {
+  if (t0 + wave < t1) {
 #pragma unroll
-    for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(wave, kc);
+    for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(t0 + wave, kc);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -293,19 +301,28 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   const int pidx = plane_index(smp & 15, m);
   // Saved planes of this (block, state group): alpha'_t and beta'_t for every
   // step, x_K, then, when K spans several rounds, S_r for every round r.
-  const int nchunks = (K + kChunk - 1) / kChunk;
+  const int nchunks = (K + kChunk - 1) / kChunk;  // rounds of the whole history
   const size_t blk_stride = (size_t)saved_planes(K) * kPlane;
   float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
   float x = 0.f, c = 0.f;
+  // A chunked history (mode 2) starts from the state the carry pass left in
+  // the chunk's second S plane, and scales its S_r by the product of every
+  // later chunk's gates (the first S plane).  Read before anything is written.
+  float suffix = 1.f;
+  if (mode == 2 && scanner) {
+    x = sv[(size_t)(2 * K + 2 + r0) * kPlane + pidx];
+    suffix = sv[(size_t)(2 * K + 1 + r0) * kPlane + pidx];
+  }
   const float mstab = stab != nullptr ? stab[0] : 1.f;
   float G[kChunk], U[kChunk];
   float Gr[kRegRounds];  // gate product of each round (rounds >= kRegRounds park theirs in saved)
 #pragma unroll
   for (int i = 0; i < kRegRounds; ++i) Gr[i] = 1.f;
 
-  for (int ch = 0; ch < nchunks; ++ch) {
+  for (int ch = r0; ch < r1; ++ch) {
+    const int lr = ch - r0;  // round within this chunk
     const int t = ch * kChunk + wave;
-    if (t < K) {
+    if (t < t1) {
       v4f acca = {0.f, 0.f, 0.f, 0.f};
       v4f accb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -326,7 +343,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
       // next round's first loads go out before this round's exchange and scan
-      if (t + kChunk < K) {
+      if (t + kChunk < t1) {
 #pragma unroll
         for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(t + kChunk, kc);
       }
@@ -341,13 +358,13 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
 
     if (scanner) {
       const int idx = smp * kGroup + m;
-      if (ch == 0) {
+      if (ch == r0) {
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kFwdWaves; ++w) s += sC[w][idx];
         c = s;
       }
-      const int tn = min(kChunk, K - ch * kChunk);
+      const int tn = min(kChunk, t1 - ch * kChunk);
 #pragma unroll
       for (int tt = 0; tt < kChunk; ++tt) {
         if (tt < tn) {
@@ -370,22 +387,25 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
       // gates, alpha'_t = beta'_t * u_t.  The full terms are
       // beta_t = S_r beta'_t and alpha_t = S_r alpha'_t with S_r the product
       // of every gate of the later rounds; the backward applies S_r.
+      // (the summary pass of a chunked history keeps only the gate products)
       float P = c, gp = 1.f;
 #pragma unroll
       for (int tt = kChunk - 1; tt >= 0; --tt) {
         if (tt < tn) {
           const int tg = ch * kChunk + tt;
-          st_stream(&sv[(size_t)(2 * tg) * kPlane + pidx], P * U[tt]);
-          st_stream(&sv[(size_t)(2 * tg + 1) * kPlane + pidx], P);
+          if (mode != 1) {
+            st_stream(&sv[(size_t)(2 * tg) * kPlane + pidx], P * U[tt]);
+            st_stream(&sv[(size_t)(2 * tg + 1) * kPlane + pidx], P);
+          }
           P *= G[tt];
           gp *= G[tt];
         }
       }
       if (nchunks > 1) {
-        if (ch < kRegRounds) {
+        if (lr < kRegRounds) {
 #pragma unroll
           for (int i = 0; i < kRegRounds; ++i)
-            if (i == ch) Gr[i] = gp;
+            if (i == lr) Gr[i] = gp;
         } else {
           sv[(size_t)(2 * K + 1 + ch) * kPlane + pidx] = gp;  // read back below, same thread
         }
@@ -396,20 +416,45 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
 
   if (!scanner) return;
 
-  const int b_glob = blk * kBlock + smp;
-  if (b_glob < B) st_stream(&ctx[(size_t)b_glob * D + sg * kGroup + m], c * x);
-  st_stream(&sv[(size_t)(2 * K) * kPlane + pidx], x);
-
-  // S_r = product of the gates of rounds r+1 .. last (S_last = 1).
-  if (nchunks > 1) {
-    float S = 1.f;
-    for (int ch = nchunks - 1; ch >= 0; --ch) {
-      float* ps = &sv[(size_t)(2 * K + 1 + ch) * kPlane + pidx];
+  if (mode == 1) {
+    // summary of this chunk for the carry pass: the product of its gates
+    // (first S plane) and its final state from x = 0 (second S plane)
+    float G_all = 1.f;
+    for (int ch = r0; ch < r1; ++ch) {
+      const int lr = ch - r0;
       float g = 1.f;
-      if (ch < kRegRounds) {
+      if (lr < kRegRounds) {
 #pragma unroll
         for (int i = 0; i < kRegRounds; ++i)
-          if (i == ch) g = Gr[i];
+          if (i == lr) g = Gr[i];
+      } else {
+        g = sv[(size_t)(2 * K + 1 + ch) * kPlane + pidx];
+      }
+      G_all *= g;
+    }
+    sv[(size_t)(2 * K + 1 + r0) * kPlane + pidx] = G_all;
+    sv[(size_t)(2 * K + 2 + r0) * kPlane + pidx] = x;
+    return;
+  }
+
+  if (cidx == C - 1) {
+    const int b_glob = blk * kBlock + smp;
+    if (b_glob < B) st_stream(&ctx[(size_t)b_glob * D + sg * kGroup + m], c * x);
+    st_stream(&sv[(size_t)(2 * K) * kPlane + pidx], x);
+  }
+
+  // S_r = product of the gates of rounds r+1 .. last (S_last = 1): this
+  // chunk's later rounds, times every later chunk's gates.
+  if (nchunks > 1) {
+    float S = suffix;
+    for (int ch = r1 - 1; ch >= r0; --ch) {
+      const int lr = ch - r0;
+      float* ps = &sv[(size_t)(2 * K + 1 + ch) * kPlane + pidx];
+      float g = 1.f;
+      if (lr < kRegRounds) {
+#pragma unroll
+        for (int i = 0; i < kRegRounds; ++i)
+          if (i == lr) g = Gr[i];
       } else {
         g = *ps;
       }
@@ -419,12 +464,41 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   }
 }
 
+// Carry across the chunks of a chunked history, one thread per (sample,
+// state) entry of a (block, state group): from each chunk's summary
+// (G_c = product of its gates, X_c = its final state from 0; first and second
+// S plane of its first round) to the state it starts from,
+//   x_start(0) = 0,  x_start(c+1) = G_c x_start(c) + X_c,
+// (second S plane) and the product of every later chunk's gates (first).
+__global__ __launch_bounds__(256) void fwd_carry_kernel(int NBG, int K, int L, int C, float* __restrict__ saved) {
+  const int bg = blockIdx.x;  // (block, state group)
+  if (bg >= NBG) return;
+  const int e = threadIdx.x;  // entry of the 16 x 16 plane
+  float* sv = saved + (size_t)bg * saved_planes(K) * kPlane + e;
+  float x = 0.f;
+  for (int cc = 0; cc < C; ++cc) {
+    float* p1 = sv + (size_t)(2 * K + 2 + cc * L / kChunk) * kPlane;
+    const float Gc = sv[(size_t)(2 * K + 1 + cc * L / kChunk) * kPlane];
+    const float Xc = *p1;
+    *p1 = x;
+    x = Gc * x + Xc;
+  }
+  float S = 1.f;
+  for (int cc = C - 1; cc >= 0; --cc) {
+    float* p0 = sv + (size_t)(2 * K + 1 + cc * L / kChunk) * kPlane;
+    const float Gc = *p0;
+    *p0 = S;
+    S *= Gc;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Backward, phase 1: split-K partial products.
 //   grid = 8 * V * ceil(P / 8), V = (SH2/64) * NG variants, 512 threads.
 // Work-group w: XCD w % 8, variant v = (w/8) % V (column block jb, state
-// group sg), slice p = ((w/8) / V) * 8 + w % 8 covering sample blocks
-// [p*BPW, min(NB, (p+1)*BPW)).
+// group sg), slice p = ((w/8) / V) * 8 + w % 8 covering units
+// [p*UPW, min(NB*(K+1), (p+1)*UPW)), unit u = (block u / (K+1), step u % (K+1)),
+// so a long history with few samples still spreads over many work-groups.
 //
 // MFMA roles (v_mfma_f32_16x16x4_f32, D[M=16][N=16] += A[16][4] B[4][16]):
 //   M = features jb*64 + 4*row + q (four M tiles q share one float4 load),
@@ -447,7 +521,7 @@ struct BwdUnit {
 
 template <class T>
 struct BwdCtx {
-  int B, K, SH2, D, NG, sg, blk0, col, state, kg;
+  int B, K, SH2, D, NG, sg, u0, col, state, kg;  // u0: first unit of the slice
   const T* H;
   const T* hs2;
   const float* saved;
@@ -464,9 +538,9 @@ struct BwdCtx {
 template <class T>
 __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, int lane) {
   const int KU = c.K + 1;
-  const int bi = u / KU;
-  const int t = u - bi * KU;
-  const int blk = c.blk0 + bi;
+  const int ug = c.u0 + u;
+  const int blk = ug / KU;
+  const int t = ug - blk * KU;
   const int sbase = blk * kBlock + 4 * c.kg;
   const bool step = t < c.K;
   const float* sv = c.saved + ((size_t)blk * c.NG + c.sg) * c.blk_stride + 4 * lane;
@@ -491,9 +565,10 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, int u, const Ctx& 
                                             float* __restrict__ d_a_out, float* __restrict__ d_b_out,
                                             float* __restrict__ d_c_out, bool write_dbg) {
   const int KU = c.K + 1;
-  const int bi = u / KU;
-  const int t = u - bi * KU;
-  const int sbase = (c.blk0 + bi) * kBlock + 4 * c.kg;
+  const int ug = c.u0 + u;
+  const int blk = ug / KU;
+  const int t = ug - blk * KU;
+  const int sbase = blk * kBlock + 4 * c.kg;
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   if (t < c.K) {
 #pragma unroll
@@ -530,7 +605,7 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, int u, const Ctx& 
 
 template <class T>
 __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
-    int B, int K, int SH2, int NG, int NB, int P, int BPW,
+    int B, int K, int SH2, int NG, int NB, int P, int UPW,
     const T* __restrict__ H, const T* __restrict__ hs2,
     const float* __restrict__ saved, const float* __restrict__ dctx,
     float* __restrict__ d_a_out, float* __restrict__ d_b_out, float* __restrict__ d_c_out,
@@ -561,7 +636,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   c.D = NG * kGroup;
   c.NG = NG;
   c.sg = sg;
-  c.blk0 = p * BPW;
+  c.u0 = p * UPW;
   c.col = jb * kColBlock + 4 * m;
   c.state = sg * kGroup + m;
   c.kg = kg;
@@ -571,8 +646,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   c.dctx = dctx;
   c.blk_stride = (size_t)saved_planes(K) * kPlane;
   c.rounds = K > kChunk;
-  const int nblk = min(NB - c.blk0, BPW);
-  const int n = nblk * (K + 1);
+  const int n = min(NB * (K + 1) - c.u0, UPW);
 
   v4f acc[4][3];
 #pragma unroll
@@ -1061,7 +1135,7 @@ __global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
 // Host side: shape checks and launch plans.
 struct Plan {
   int B, K, SH2, D, NG, NB, NJB, V;
-  int P, BPW;
+  int P, UPW;  // backward slices and units per slice
   size_t saved_bytes, ws_bytes;
 };
 
@@ -1082,13 +1156,16 @@ int make_plan(int B, int K, int SH2, int D, Plan* pl) {
   if ((long long)pl->NB * K > (1LL << 30)) return MAMBA2_SCAN_EBADDIM;
   pl->NJB = SH2 / kColBlock;
   pl->V = pl->NJB * pl->NG;
+  // Backward slices: about kBwdTargetGroups work-groups over the V variants,
+  // each slice at least one unit per wave.
+  const int units = pl->NB * (K + 1);
   int p0 = (kBwdTargetGroups + pl->V - 1) / pl->V;
-  if (p0 > pl->NB) p0 = pl->NB;
-  pl->BPW = (pl->NB + p0 - 1) / p0;
-  pl->P = (pl->NB + pl->BPW - 1) / pl->BPW;
+  if (p0 > (units + kBwdWaves - 1) / kBwdWaves) p0 = (units + kBwdWaves - 1) / kBwdWaves;
+  pl->UPW = (units + p0 - 1) / p0;
+  pl->P = (units + pl->UPW - 1) / pl->UPW;
   pl->saved_bytes = (size_t)pl->NB * pl->NG * (size_t)saved_planes(K) * kPlane * sizeof(float);
   // Sized for p0 >= P slices: p0 never decreases as B grows, so neither does
-  // the workspace (P itself can, when BPW steps up).
+  // the workspace (P itself can, when UPW steps up).
   pl->ws_bytes = (size_t)pl->NG * p0 * (size_t)SH2 * 3 * kGroup * sizeof(float);
   return MAMBA2_SCAN_OK;
 }
@@ -1100,12 +1177,43 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? MAMBA2_SCAN_OK : MAMBA2_SCAN_EHIP;
 }
 
+// History chunks for the forward: with few sample blocks and a long history
+// the chunks of one block run in parallel (a summary pass, the carry, then
+// the full pass per chunk).  Chunks are whole pairs of rounds, and the last
+// one spans at least two rounds (its summary needs two S planes).
+void fwd_chunks(const Plan& pl, int* L, int* C) {
+  *L = pl.K;
+  *C = 1;
+  const long long wgs = (long long)pl.NB * pl.NG;
+  if (pl.K < 4 * kChunk || wgs >= kFwdChunkTarget / 2) return;
+  long long c = (kFwdChunkTarget + wgs - 1) / wgs;
+  if (c > pl.K / (2 * kChunk)) c = pl.K / (2 * kChunk);
+  if (c < 2) return;
+  int l = (int)((pl.K + c - 1) / c);
+  l = ((l + 2 * kChunk - 1) / (2 * kChunk)) * (2 * kChunk);
+  int cc = (pl.K + l - 1) / l;
+  if (pl.K - (cc - 1) * l <= kChunk) cc -= 1;
+  if (cc < 2) return;
+  *L = l;
+  *C = cc;
+}
+
 template <int NKC, class T>
 void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const float* WB,
                 const float* WC, const float* stab, float* ctx, float* saved, hipStream_t st) {
-  const int grid = 8 * pl.NG * ((pl.NB + 7) / 8);
+  int L, C;
+  fwd_chunks(pl, &L, &C);
+  const int grid = 8 * pl.NG * C * ((pl.NB + 7) / 8);
+  if (C == 1) {
+    hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB,
+                       H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 0);
+    return;
+  }
   hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
-                     hs2, WA, WB, WC, stab, ctx, saved);
+                     hs2, WA, WB, WC, stab, ctx, saved, L, C, 1);
+  hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG), dim3(kPlane), 0, st, pl.NB * pl.NG, pl.K, L, C, saved);
+  hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
+                     hs2, WA, WB, WC, stab, ctx, saved, L, C, 2);
 }
 
 int check_bwd_common(const Plan& pl, const void* H, const void* hs2, const void* saved, size_t saved_bytes,
@@ -1132,7 +1240,7 @@ void launch_partials(const Plan& pl, const T* H, const T* hs2, const void* saved
                      float* da, float* db, float* dc, void* ws, hipStream_t st) {
   const int grid = 8 * pl.V * ((pl.P + 7) / 8);
   hipLaunchKernelGGL(bwd_partials_kernel<T>, dim3(grid), dim3(kBwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
-                     pl.NB, pl.P, pl.BPW, H, hs2, static_cast<const float*>(saved), dctx, da, db, dc,
+                     pl.NB, pl.P, pl.UPW, H, hs2, static_cast<const float*>(saved), dctx, da, db, dc,
                      static_cast<float*>(ws));
 }
 

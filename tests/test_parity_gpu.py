@@ -250,3 +250,47 @@ def test_graph_replays_match_eager():
         assert np.array_equal(ctx.cpu().numpy().view(np.uint32), eager["context"].view(np.uint32)), rep
         for k in ("dW_A", "dW_B", "dW_C"):
             assert np.array_equal(out[k].cpu().numpy().view(np.uint32), eager[k].view(np.uint32)), (rep, k)
+
+
+# Long histories with few samples: the forward splits the history into chunks
+# that run in parallel (summary pass, carry across chunks, full pass).  Shapes
+# chosen so the chunked path is taken, with long-memory gates (+2 logit shift)
+# so that carries across chunk boundaries matter.
+LONG_FEW_SHAPES = [
+    (64, 1024, 256, 16),
+    (8, 2048, 128, 32),
+    (3, 300, 64, 64),
+    (17, 160, 192, 16),
+]
+
+
+@pytest.mark.parametrize("B,K,SH2,D", LONG_FEW_SHAPES, ids=lambda v: str(v))
+def test_chunked_history(B, K, SH2, D):
+    inputs = make_inputs(B, K, SH2, D, seed=B + K, gate_bias=2.0)
+    got, f, _ = check_against_oracle(inputs, debug=True)
+    assert 0.8 < float(np.mean(f.g)) < 0.95  # long memory: the carry spans many chunks
+
+
+def test_chunked_history_blend_and_input_grads():
+    """The chunked forward with the stability multiplier feeds the blend backward and the input gradients."""
+    from tests.inputs import blend_extras
+    inputs = make_inputs(32, 512, 128, 16, seed=9, gate_bias=2.0)
+    extras = blend_extras(32, 128, 9)
+    t = _to_dev(inputs)
+    dev = t["h_s2"].device
+    stab = torch.tensor([0.97], device=dev)
+    w = torch.from_numpy(extras["temporal_weight"]).to(dev)
+    dhe = torch.from_numpy(extras["d_h_enriched"]).to(dev)
+    ctx, he, saved = m2.fwd_blend(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], stability=stab,
+                                  temporal_weight=w)
+    g = m2.bwd_blend(t["h_history"], t["h_s2"], saved, dhe, 16, temporal_weight=w)
+    dH, dhs2 = m2.bwd_input(t["W_A"], t["W_B"], t["W_C"], saved, g["d_context"], 512)
+    torch.cuda.synchronize()
+    f, he_ref, bb, b = orc.fwd_bwd_blend(inputs, 0.97, extras["temporal_weight"], extras["d_h_enriched"])
+    assert_elementwise(ctx.cpu().numpy(), f.context, "context")
+    assert_elementwise(he.cpu().numpy(), he_ref, "h_enriched")
+    for name in ("dW_A", "dW_B", "dW_C"):
+        assert_l1(g[name].cpu().numpy(), getattr(b, name), name)
+    ig = orc.input_grads(b, inputs["W_A"], inputs["W_B"], inputs["W_C"])
+    assert_elementwise(dH.cpu().numpy(), ig.d_h_history, "d_h_history")
+    assert_elementwise(dhs2.cpu().numpy(), ig.d_h_s2, "d_h_s2")
