@@ -423,6 +423,41 @@ def main():
     for st_ in sets:
         del st_["h16"], st_["hs16"]
 
+    # ---- a long history with few samples (chunked forward), its own rotation
+    def workload_step_us(name):
+        wl = WORKLOADS[name]
+        base_in = {k: torch.from_numpy(v).to(dev) for k, v in workload_inputs(name).items()}
+        wsets = []
+        for _ in range(R):
+            x = {k: v.clone() for k, v in base_in.items()}
+            x["context"] = torch.empty((wl.B, wl.D), device=dev)
+            x["saved"] = m2.alloc_saved(wl.B, wl.K, wl.SH2, wl.D, dev)
+            x["ws"] = m2.alloc_workspace(wl.B, wl.K, wl.SH2, wl.D, dev)
+            x["dW"] = [torch.empty((wl.SH2, wl.D), device=dev) for _ in range(3)]
+            wsets.append(x)
+        del base_in
+
+        def wstep(i):
+            a = wsets[i % R]
+            m2.fwd(a["h_history"], a["h_s2"], a["W_A"], a["W_B"], a["W_C"], context=a["context"], saved=a["saved"])
+            bset = wsets[(i - R // 2) % R]
+            m2.bwd_partials(bset["h_history"], bset["h_s2"], bset["saved"], bset["d_context"], bset["ws"])
+            m2.bwd_reduce(wl.B, wl.K, wl.SH2, wl.D, bset["ws"], *bset["dW"])
+
+        for i in range(R):
+            a = wsets[i]
+            m2.fwd(a["h_history"], a["h_s2"], a["W_A"], a["W_B"], a["W_C"], context=a["context"], saved=a["saved"])
+        us = graph_us(wstep, R)
+        wbytes, _ = algorithmic_bytes(wl.B, wl.K, wl.SH2, wl.D)
+        del wsets
+        torch.cuda.empty_cache()
+        gbps = wbytes / (us * 1e-6) / 1e9
+        return {"workload": name, "B": wl.B, "K": wl.K, "SH2": wl.SH2, "STATE_D": wl.D, "us": round(us, 2),
+                "algorithmic_bytes": wbytes, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBS, 4)}
+
+    long_few = workload_step_us("long_few") if args.workload == "pages_shape" else None
+
     # ---- copy ceiling: a 1 GiB device-to-device copy (read + write bytes)
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -493,6 +528,8 @@ def main():
         "kernel_us": {n: round(kern_us[n], 2) for n in names},
         "roofline": roof,
         # not part of the step: the optional input gradients, timed the same way
+        # another workload's step, same cold protocol: a long history with few samples
+        "long_few_step": long_few,
         # the same step with bf16 h_history and h_s2 (fp32 arithmetic): not the headline
         "bf16_step": {"us": round(bf16_step_us, 2), "algorithmic_bytes": bf16_bytes,
                       "achieved": round(bf16_gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -36,15 +36,17 @@ class Workload:
     gate_bias: float = 0.0  # added to W_A[0, :] with h_history[:, :, 0] = 1
 
 
-# The five workloads: a tiny case the oracle finishes instantly, a mid case,
-# the pages' own shape (B=8192, K=8, SH2=256, STATE_D=16), a long history
-# with long-memory gates, and a wide state.
+# The workloads: a tiny case the oracle finishes instantly, a mid case, the
+# pages' own shape (B=8192, K=8, SH2=256, STATE_D=16), a long history with
+# long-memory gates, a wide state, and a long history with few samples.
 WORKLOADS = {
     "tiny": Workload("tiny", 64, 8, 256, 16, seed=0),
     "mid": Workload("mid", 1024, 8, 256, 16, seed=1),
     "pages_shape": Workload("pages_shape", 8192, 8, 256, 16, seed=2),
     "long_history": Workload("long_history", 8192, 64, 256, 16, seed=3, gate_bias=2.0),
     "wide_state": Workload("wide_state", 32768, 8, 512, 64, seed=4),
+    # a long history with few samples (the forward runs its chunks in parallel)
+    "long_few": Workload("long_few", 128, 2048, 256, 16, seed=5, gate_bias=2.0),
 }
 
 

@@ -108,10 +108,10 @@ def test_workload_full(name):
     check_against_oracle(workload_inputs(name), debug=(name != "pages_shape"))
 
 
-@pytest.mark.parametrize("name", ["long_history", "wide_state"])
+@pytest.mark.parametrize("name", ["long_history", "wide_state", "long_few"])
 def test_workload_large(name):
     got, f, _ = check_against_oracle(workload_inputs(name), debug=False)
-    if name == "long_history":
+    if name in ("long_history", "long_few"):
         # the +2 logit shift gives long-memory gates
         assert 0.8 < float(np.mean(f.g)) < 0.95
 
