@@ -1,6 +1,6 @@
 """Benchmark: ms per Mamba2 scan fwd+bwd step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload pages_shape]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload pages_shape] [--no-extras]
 
 One step = mamba2_scan_fwd + mamba2_scan_bwd (partials + reduce) over one
 batch of seeded synthetic input already resident in HBM.  Prints one JSON line.
@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--workload", default="pages_shape")
     ap.add_argument("--sets", type=int, default=8, help="rotating input sets (even, >= 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the blend, bf16 and long_few measurements (keeps a profile to the headline kernels)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -352,50 +354,8 @@ def main():
         kern_us[name] = e0.elapsed_time(e1) * 1e3 / n_launch
         del g
 
-    # ---- the blend path (optional step after the path): cold rotation of
-    # fwd_blend(set s) + bwd_blend(set s - R/2), timed like the headline
-    def blend_step(i):
-        fwd_blend(sets[i % R])
-        bwd_blend(sets[(i - R // 2) % R])
-
-    with torch.cuda.stream(stream):
-        for i in range(R):
-            blend_step(i)
-        torch.cuda.synchronize()
-        bg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(bg, stream=stream):
-            for i in range(R):
-                blend_step(i)
-        torch.cuda.synchronize()
-        bg.replay()
-        reps = max(2, args.steps // R)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            bg.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    blend_step_us = e0.elapsed_time(e1) * 1e3 / (reps * R)
-    del bg
-
-    # ---- bf16 trunk inputs (the *_bf16 entry points), same cold rotation
-    for st_ in sets:
-        st_["h16"] = st_["h_history"].to(torch.bfloat16)
-        st_["hs16"] = st_["h_s2"].to(torch.bfloat16)
-
-    def fwd16(s):
-        m2.fwd(s["h16"], s["hs16"], s["W_A"], s["W_B"], s["W_C"], context=s["context"], saved=s["saved"])
-
-    def partials16(s):
-        m2.bwd_partials(s["h16"], s["hs16"], s["saved"], s["d_context"], s["ws"])
-
-    def step16(i):
-        fwd16(sets[i % R])
-        sb = sets[(i - R // 2) % R]
-        partials16(sb)
-        reduce(sb)
-
+    # ---- optional paths (not the step): each timed as a cold rotation replayed
+    # from one captured graph
     def graph_us(fn_step, count):
         with torch.cuda.stream(stream):
             for i in range(count):
@@ -417,11 +377,24 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / (reps * count)
 
-    bf16_step_us = graph_us(step16, R)
-    bf16_kern_us = {"fwd_kernel": graph_us(lambda i: fwd16(sets[i % R]), 8 * R),
-                    "bwd_partials_kernel": graph_us(lambda i: partials16(sets[i % R]), 8 * R)}
-    for st_ in sets:
-        del st_["h16"], st_["hs16"]
+
+    # the blend path: fwd_blend(set s) + bwd_blend(set s - R/2)
+    def blend_step(i):
+        fwd_blend(sets[i % R])
+        bwd_blend(sets[(i - R // 2) % R])
+
+    # bf16 trunk inputs (the *_bf16 entry points)
+    def fwd16(s):
+        m2.fwd(s["h16"], s["hs16"], s["W_A"], s["W_B"], s["W_C"], context=s["context"], saved=s["saved"])
+
+    def partials16(s):
+        m2.bwd_partials(s["h16"], s["hs16"], s["saved"], s["d_context"], s["ws"])
+
+    def step16(i):
+        fwd16(sets[i % R])
+        sb = sets[(i - R // 2) % R]
+        partials16(sb)
+        reduce(sb)
 
     # ---- a long history with few samples (chunked forward), its own rotation
     def workload_step_us(name):
@@ -456,7 +429,21 @@ def main():
                 "algorithmic_bytes": wbytes, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBS, 4)}
 
-    long_few = workload_step_us("long_few") if args.workload == "pages_shape" else None
+    blend_step_us = bf16_step_us = None
+    bf16_kern_us = {}
+    long_few = None
+    if not args.no_extras:
+        blend_step_us = graph_us(blend_step, R)
+        for st_ in sets:
+            st_["h16"] = st_["h_history"].to(torch.bfloat16)
+            st_["hs16"] = st_["h_s2"].to(torch.bfloat16)
+        bf16_step_us = graph_us(step16, R)
+        bf16_kern_us = {"fwd_kernel": graph_us(lambda i: fwd16(sets[i % R]), 8 * R),
+                        "bwd_partials_kernel": graph_us(lambda i: partials16(sets[i % R]), 8 * R)}
+        for st_ in sets:
+            del st_["h16"], st_["hs16"]
+        if args.workload == "pages_shape":
+            long_few = workload_step_us("long_few")
 
     # ---- copy ceiling: a 1 GiB device-to-device copy (read + write bytes)
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -476,10 +463,20 @@ def main():
     del src, dst
 
     step_bytes, per_kernel_bytes = algorithmic_bytes(B, K, SH2, D)
-    blend_gbps = per_kernel_bytes["blend_step"] / (blend_step_us * 1e-6) / 1e9
     # bf16 trunk inputs: h_history and h_s2 move half the bytes, twice per step
     bf16_bytes = step_bytes - (B * K * SH2 + B * SH2) * 4
-    bf16_gbps = bf16_bytes / (bf16_step_us * 1e-6) / 1e9
+    blend_out = bf16_out = None
+    if blend_step_us is not None:
+        blend_gbps = per_kernel_bytes["blend_step"] / (blend_step_us * 1e-6) / 1e9
+        blend_out = {"us": round(blend_step_us, 2), "stability": BLEND_STABILITY,
+                     "temporal_weight": "U(0.5, 1.5)", "algorithmic_bytes": per_kernel_bytes["blend_step"],
+                     "achieved": round(blend_gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(blend_gbps / HBM_PEAK_GBS, 4)}
+        bf16_gbps = bf16_bytes / (bf16_step_us * 1e-6) / 1e9
+        bf16_out = {"us": round(bf16_step_us, 2), "algorithmic_bytes": bf16_bytes,
+                    "achieved": round(bf16_gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(bf16_gbps / HBM_PEAK_GBS, 4),
+                    "kernel_us": {k: round(v, 2) for k, v in bf16_kern_us.items()}}
     flops, per_kernel_flops = algorithmic_flops(B, K, SH2, D)
     dom = max(names, key=lambda n: kern_us[n])
     hbm_us = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
@@ -531,15 +528,9 @@ def main():
         # another workload's step, same cold protocol: a long history with few samples
         "long_few_step": long_few,
         # the same step with bf16 h_history and h_s2 (fp32 arithmetic): not the headline
-        "bf16_step": {"us": round(bf16_step_us, 2), "algorithmic_bytes": bf16_bytes,
-                      "achieved": round(bf16_gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": round(bf16_gbps / HBM_PEAK_GBS, 4),
-                      "kernel_us": {k: round(v, 2) for k, v in bf16_kern_us.items()}},
+        "bf16_step": bf16_out,
         # not part of the step either: the blend path, fwd_blend + bwd_blend, cold rotation
-        "blend_step": {"us": round(blend_step_us, 2), "stability": BLEND_STABILITY,
-                       "temporal_weight": "U(0.5, 1.5)", "algorithmic_bytes": per_kernel_bytes["blend_step"],
-                       "achieved": round(blend_gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": round(blend_gbps / HBM_PEAK_GBS, 4)},
+        "blend_step": blend_out,
         "input_grads": {"kernel": "dinput_kernel", "us": round(kern_us["dinput_kernel"], 2), "bound": "hbm",
                         "achieved": round(per_kernel_bytes["dinput_kernel"] / (kern_us["dinput_kernel"] * 1e-6) / 1e9, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
