@@ -116,6 +116,18 @@ __device__ __forceinline__ v4f ld4_in<bf16_t>(const bf16_t* p) {
   r[3] = __uint_as_float(w[1] & 0xffff0000u);
   return r;
 }
+// Buffer descriptor over `bytes` bytes at `base` (gfx9: 32-bit data format);
+// accesses past the end are dropped by the hardware range check.
+constexpr unsigned kBufWord3 = 0x00020000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufWord3);
+}
+// 16-byte store written through to memory (cache policy sc0 | sc1: system
+// scope), leaving no dirty L2 line behind.
+constexpr int kWriteThrough = 0x11;
+__device__ __forceinline__ void st4_through(__amdgpu_buffer_rsrc_t rs, unsigned off, v4f v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rs, off, 0, kWriteThrough);
+}
 __device__ __forceinline__ void st4_stream(float* p, v4f v) {
   __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
 }
@@ -610,7 +622,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
     const float* __restrict__ saved, const float* __restrict__ dctx,
     float* __restrict__ d_a_out, float* __restrict__ d_b_out, float* __restrict__ d_c_out,
     float* __restrict__ ws) {
-  __shared__ float sRed[kBwdWaves][3 * kColBlock * kGroup];
+  __shared__ __attribute__((aligned(16))) float sRed[kBwdWaves][3 * kColBlock * kGroup];
 
   const int NJB = SH2 / kColBlock;
   const int V = NJB * NG;
@@ -683,13 +695,16 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
         sRed[wave][pl * (kColBlock * kGroup) + (16 * kg + 4 * r + q) * kGroup + m] = acc[q][pl][r];
   __syncthreads();
 
-  // Slice layout: ws[sg][p][jb][plane][jl][n].
+  // Slice layout: ws[sg][p][jb][plane][jl][n].  Written through to memory
+  // (16-byte stores with system-scope coherence) so that no dirty L2 lines
+  // remain to be written back before the reduce can start.
   float* out = ws + ((size_t)sg * P + p) * ((size_t)SH2 * 3 * kGroup) + (size_t)jb * (3 * kColBlock * kGroup);
-  for (int e = tid; e < 3 * kColBlock * kGroup; e += kBwdWaves * 64) {
-    float s = sRed[0][e];
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(out, 3 * kColBlock * kGroup * sizeof(float));
+  for (int e = 4 * tid; e < 3 * kColBlock * kGroup; e += 4 * kBwdWaves * 64) {
+    v4f s = *reinterpret_cast<const v4f*>(&sRed[0][e]);
 #pragma unroll
-    for (int w = 1; w < kBwdWaves; ++w) s += sRed[w][e];
-    st_stream(&out[e], s);
+    for (int w = 1; w < kBwdWaves; ++w) s += *reinterpret_cast<const v4f*>(&sRed[w][e]);
+    st4_through(rs, (unsigned)(e * sizeof(float)), s);
   }
 }
 
@@ -890,7 +905,6 @@ constexpr int kDinWaves = 4;
 constexpr int kDinTargetWGs = 4096 / kDinWaves;      // 16 resident waves per CU
 constexpr int kDinRow = kColBlock + 4;               // padded LDS row of the output transpose
 constexpr int kDinPlaneLds = kPlane + 16;            // padded LDS copy of a saved plane
-constexpr unsigned kBufWord3 = 0x00020000u;          // gfx9 buffer descriptor: 32-bit data format
 constexpr long long kDinMaxRowFloats = 1LL << 26;    // K * SH2 limit: 16 rows of samples stay below 4 GiB
 
 // LDS floats of one wave's tile: the unit's planes (alpha', beta', S_r,
@@ -965,9 +979,7 @@ struct DinW {
   }
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t din_rsrc(float* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufWord3);
-}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t din_rsrc(float* base, unsigned bytes) { return make_rsrc(base, bytes); }
 
 template <int NGT, bool ROUNDS, class WOps>
 __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const DinCtx& c, int SH2, int jb, int kg,
