@@ -8,10 +8,13 @@ batch of seeded synthetic input already resident in HBM.  Prints one JSON line.
 Cold protocol (the headline): R input sets rotate so that no step's reads
 can be served from the 256 MB Infinity Cache.  Step s runs the forward of
 set s % R and the backward of set (s - R/2) % R, so between a set's forward
-and its backward R/2 other steps stream far more than the cache holds.  A
+and its backward R/2 other steps stream far more than the cache holds.
 The K timed steps are replays of captured HIP graphs (a whole number of
 rotations per graph, up to 200 steps, plus one graph for the remainder),
-bracketed by device synchronisation.
+bracketed by device synchronisation.  A graph's first replay costs more
+than later ones (about 3 us per step for 200 steps), so after the W warmup
+steps each timed graph is replayed once untimed; that replay's time is
+reported as first_replay_ms_per_step.
 
 Per-kernel durations come from HIP events (on the stream the kernels run on)
 around a captured batch of back-to-back launches of one kernel that walks the
@@ -284,6 +287,13 @@ def main():
 
     run_steps(args.warmup)
     torch.cuda.synchronize()
+    # first replay of each timed graph, untimed (one-time launch cost)
+    tf = time.perf_counter()
+    big.replay()
+    if rest is not None:
+        rest.replay()
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - tf) * 1e3 / (chunk + rem)
     t0 = time.perf_counter()
     for _ in range(n_big):
         big.replay()
@@ -522,6 +532,7 @@ def main():
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "achieved_over_copy_ceiling": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / copy_gbps, 4),
         "warm_ms_per_step": round(warm_ms, 5),
+        "first_replay_ms_per_step": round(first_ms, 5),
         "kernel_us": {n: round(kern_us[n], 2) for n in names},
         "roofline": roof,
         # not part of the step: the optional input gradients, timed the same way

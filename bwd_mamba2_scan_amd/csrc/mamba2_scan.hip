@@ -29,7 +29,7 @@
 //    pass over earlier rounds' terms is ever needed.
 //
 //  * bwd_partials_kernel: split-K tall reduction.  One work-group per
-//    (64-feature column block, state group, range of sample blocks); its 8
+//    (64-feature column block, state group, range of sample blocks); its 12
 //    waves take (sample block, history step) units round-robin and accumulate
 //    H^T [d_a | d_b] and h_s2^T d_c with MFMA (M = features, N = states,
 //    K = rows) in registers.  The waves' partials are summed in LDS in a fixed
@@ -60,7 +60,7 @@ constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
 constexpr int kFwdPrefetch = 6;    // history loads each forward wave keeps in flight
 constexpr int kRegRounds = 8;      // rounds whose gate product the forward keeps in registers
 constexpr int kFwdChunkTarget = 512;  // forward work-groups a chunked history aims for
-constexpr int kBwdWaves = 8;
+constexpr int kBwdWaves = 12;
 constexpr int kBwdTargetGroups = 256;  // backward work-groups to aim for (one per CU)
 constexpr int kRedThreads = 256;
 constexpr int kRedQuads = 32;      // output float4s per reduce work-group
@@ -506,7 +506,9 @@ __global__ __launch_bounds__(256) void fwd_carry_kernel(int NBG, int K, int L, i
 
 // ---------------------------------------------------------------------------
 // Backward, phase 1: split-K partial products.
-//   grid = 8 * V * ceil(P / 8), V = (SH2/64) * NG variants, 512 threads.
+//   grid = 8 * V * ceil(P / 8), V = (SH2/64) * NG variants, 768 threads
+//   (12 waves: three per SIMD, for the matrix cores to have work while
+//   other waves wait for memory).
 // Work-group w: XCD w % 8, variant v = (w/8) % V (column block jb, state
 // group sg), slice p = ((w/8) / V) * 8 + w % 8 covering units
 // [p*UPW, min(NB*(K+1), (p+1)*UPW)), unit u = (block u / (K+1), step u % (K+1)),
@@ -520,102 +522,111 @@ __global__ __launch_bounds__(256) void fwd_carry_kernel(int NBG, int K, int L, i
 //
 // Units: each sample block contributes K "step" units (H^T [d_a|d_b] at one
 // history step) and one "readout" unit (h_s2^T d_c).  Wave w takes units
-// w, w+8, ... (so the 8 waves of a work-group read neighbouring rows at the
+// w, w+12, ... (so the waves of a work-group read neighbouring rows at the
 // same time); each wave keeps the loads of its next unit in flight while it
-// multiplies the current one.
+// multiplies the current one.  The unit index is scalar (the wave index is
+// read as a scalar), so block, step and row bases cost scalar instructions
+// only.
 struct BwdUnit {
   v4f h[4];   // A operands: 4 rows (samples 4kg+i) x 4 features
   v4f al;     // alpha'_t (step unit) or x_K (readout unit), samples 4kg..4kg+3
   v4f be;     // beta'_t (step unit)
   v4f sr;     // S_r of the step's round (1 when K fits one round)
   float dc[4];  // d_context of samples 4kg+i, state n (unmasked)
+  int blk, t, nvalid;  // the unit's block and step (t == K: readout), samples below B
 };
 
+// Per-work-group constants, and this lane's fixed offsets.  The unit index is
+// the same for every lane of a wave, so everything that depends only on it
+// (block, step, plane, row bases) is scalar arithmetic; a lane adds its own
+// sample row (4kg), feature column and state.
 template <class T>
 struct BwdCtx {
-  int B, K, SH2, D, NG, sg, u0, col, state, kg;  // u0: first unit of the slice
+  int B, K, SH2, D, NG, sg, u0, kg, state;
   const T* H;
   const T* hs2;
   const float* saved;
   const float* dctx;
   size_t blk_stride;
   bool rounds;  // K spans more than one round: apply S_r
+  long long hk_step, hk_out;  // elements from a unit's row i to row 4kg+i: step rows, readout rows
+  int col;                    // jb*64 + 4m: first of this lane's four features
 };
+
 
 // Every unit issues the same loads, from addresses chosen by select: a step
 // unit reads alpha'_t, beta'_t, S_r and four H rows; the readout reads x_K
 // (three times) and four h_s2 rows.  With no memory operation under a branch
 // the compiler's memory-counter waits stay exact, so the next unit's loads
-// (issued before this unit is consumed) stay in flight.
+// (issued before this unit is consumed) stay in flight.  Rows of samples past
+// B (last block only) re-read a valid row; their d_context is masked to zero.
 template <class T>
 __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, int lane) {
-  const int KU = c.K + 1;
+  // unit u of the work-group's slice: block and step (t == K: the readout)
   const int ug = c.u0 + u;
-  const int blk = ug / KU;
-  const int t = ug - blk * KU;
-  const int sbase = blk * kBlock + 4 * c.kg;
-  const bool step = t < c.K;
-  const float* sv = c.saved + ((size_t)blk * c.NG + c.sg) * c.blk_stride + 4 * lane;
-  const int p0 = step ? 2 * t : 2 * c.K;
-  const int p1 = step ? 2 * t + 1 : 2 * c.K;
-  const int ps = (c.rounds && step) ? 2 * c.K + 1 + t / kChunk : 2 * c.K;  // a valid plane either way
-  U.al = ld4(sv + (size_t)p0 * kPlane);
-  U.be = ld4(sv + (size_t)p1 * kPlane);
-  U.sr = ld4(sv + (size_t)ps * kPlane);
-  const T* rows = step ? c.H + (size_t)t * c.SH2 : c.hs2;
-  const size_t rstride = step ? (size_t)c.K * c.SH2 : (size_t)c.SH2;  // floats between samples
+  BwdUnit& q = U;
+  q.blk = ug / (c.K + 1);
+  q.t = ug - q.blk * (c.K + 1);
+  q.nvalid = c.B - q.blk * kBlock;
+  const bool step = q.t < c.K;
+  const float* sv = c.saved + ((size_t)q.blk * c.NG + c.sg) * c.blk_stride;
+  const int p0 = step ? 2 * q.t : 2 * c.K;
+  const int p1 = step ? 2 * q.t + 1 : 2 * c.K;
+  const int ps = (c.rounds && step) ? 2 * c.K + 1 + q.t / kChunk : 2 * c.K;  // a valid plane either way
+  U.al = ld4(sv + (size_t)p0 * kPlane + 4 * lane);
+  U.be = ld4(sv + (size_t)p1 * kPlane + 4 * lane);
+  U.sr = ld4(sv + (size_t)ps * kPlane + 4 * lane);
+  const T* rows = step ? c.H + (size_t)q.t * c.SH2 : c.hs2;
+  const size_t rstride = step ? (size_t)c.K * c.SH2 : (size_t)c.SH2;  // elements between samples
+  const long long hk = step ? c.hk_step : c.hk_out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int sc = min(sbase + i, c.B - 1);
-    U.h[i] = ld4_in(rows + (size_t)sc * rstride + c.col);
-    U.dc[i] = c.dctx[(size_t)sc * c.D + c.state];
+    const int s0 = min(q.blk * kBlock + i, c.B - 1);  // row i of the block (scalar)
+    const bool ok = 4 * c.kg + i < q.nvalid;
+    U.h[i] = ld4_in(rows + (size_t)s0 * rstride + (ok ? hk : 0) + c.col);
+    U.dc[i] = c.dctx[(size_t)s0 * c.D + (ok ? 4 * c.kg * c.D : 0) + c.state];
   }
 }
 
-template <class Ctx>
-__device__ __forceinline__ void bwd_compute(const BwdUnit& U, int u, const Ctx& c, v4f (&acc)[4][3],
+// DBG: also store d_a, d_b, d_c (a separate instantiation, so the product
+// path carries no stores and no branches for them).
+template <bool DBG, class Ctx>
+__device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const Ctx& c, v4f (&acc)[4][3],
                                             float* __restrict__ d_a_out, float* __restrict__ d_b_out,
                                             float* __restrict__ d_c_out, bool write_dbg) {
-  const int KU = c.K + 1;
-  const int ug = c.u0 + u;
-  const int blk = ug / KU;
-  const int t = ug - blk * KU;
-  const int sbase = blk * kBlock + 4 * c.kg;
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  if (t < c.K) {
+  const BwdUnit& q = U;
+  const int sbase = q.blk * kBlock + 4 * c.kg;
+  if (q.t < c.K) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int s = sbase + i;
-      const bool ok = s < c.B;
+      const bool ok = live && 4 * c.kg + i < q.nvalid;
       const float dc = ok ? (c.rounds ? U.dc[i] * U.sr[i] : U.dc[i]) : 0.f;
       const float da = dc * U.al[i];
       const float db = dc * U.be[i];
-      const v4f h = ok ? U.h[i] : zero;
-      if (write_dbg && ok) {
-        if (d_a_out) d_a_out[((size_t)s * c.K + t) * c.D + c.state] = da;
-        if (d_b_out) d_b_out[((size_t)s * c.K + t) * c.D + c.state] = db;
+      if (DBG && write_dbg && ok) {
+        const int s = sbase + i;
+        if (d_a_out) d_a_out[((size_t)s * c.K + q.t) * c.D + c.state] = da;
+        if (d_b_out) d_b_out[((size_t)s * c.K + q.t) * c.D + c.state] = db;
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[q][0] = mfma16x16x4(h[q], da, acc[q][0]);
-        acc[q][1] = mfma16x16x4(h[q], db, acc[q][1]);
+      for (int qq = 0; qq < 4; ++qq) {
+        acc[qq][0] = mfma16x16x4(U.h[i][qq], da, acc[qq][0]);
+        acc[qq][1] = mfma16x16x4(U.h[i][qq], db, acc[qq][1]);
       }
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int s = sbase + i;
-      const bool ok = s < c.B;
+      const bool ok = live && 4 * c.kg + i < q.nvalid;
       const float dcc = (ok ? U.dc[i] : 0.f) * U.al[i];
-      const v4f h = ok ? U.h[i] : zero;
-      if (write_dbg && ok && d_c_out) d_c_out[(size_t)s * c.D + c.state] = dcc;
+      if (DBG && write_dbg && ok && d_c_out) d_c_out[(size_t)(sbase + i) * c.D + c.state] = dcc;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q][2] = mfma16x16x4(h[q], dcc, acc[q][2]);
+      for (int qq = 0; qq < 4; ++qq) acc[qq][2] = mfma16x16x4(U.h[i][qq], dcc, acc[qq][2]);
     }
   }
 }
 
-template <class T>
+template <class T, bool DBG>
 __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
     int B, int K, int SH2, int NG, int NB, int P, int UPW,
     const T* __restrict__ H, const T* __restrict__ hs2,
@@ -635,7 +646,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   const int sg = v / NJB;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: unit indices stay scalar
   const int lane = tid & 63;
   const int kg = lane >> 4;
   const int m = lane & 15;
@@ -658,6 +669,8 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   c.dctx = dctx;
   c.blk_stride = (size_t)saved_planes(K) * kPlane;
   c.rounds = K > kChunk;
+  c.hk_step = 4LL * kg * K * SH2;
+  c.hk_out = 4LL * kg * SH2;
   const int n = min(NB * (K + 1) - c.u0, UPW);
 
   v4f acc[4][3];
@@ -669,19 +682,20 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   constexpr int S = kBwdWaves;
   // Two-unit ring.  Requests are unconditional: past the last unit a wave
   // re-loads the last unit (unused), so the compiler's waits stay exact.
+  // Both halves of an iteration always run: a unit past the last one (u >= n)
+  // re-reads and re-multiplies the last unit with its d_context masked to
+  // zero, so the loop has no data-dependent exit between the two halves and
+  // each unit's registers keep one role.
   BwdUnit R0, R1;
   int u = wave;
   bwd_load(R0, min(u, n - 1), c, lane);
-  while (u < n) {
+  for (; u < n; u += 2 * S) {
     bwd_load(R1, min(u + S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
-    bwd_compute(R0, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
-    u += S;
-    if (u >= n) break;
-    bwd_load(R0, min(u + S, n - 1), c, lane);
+    bwd_compute<DBG>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    bwd_load(R0, min(u + 2 * S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
-    bwd_compute(R1, u, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
-    u += S;
+    bwd_compute<DBG>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
   }
 
   // Result lane (g = kg, n = m), element r of tile q: feature row
@@ -1251,7 +1265,8 @@ template <class T>
 void launch_partials(const Plan& pl, const T* H, const T* hs2, const void* saved, const float* dctx,
                      float* da, float* db, float* dc, void* ws, hipStream_t st) {
   const int grid = 8 * pl.V * ((pl.P + 7) / 8);
-  hipLaunchKernelGGL(bwd_partials_kernel<T>, dim3(grid), dim3(kBwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
+  auto kern = (da || db || dc) ? bwd_partials_kernel<T, true> : bwd_partials_kernel<T, false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
                      pl.NB, pl.P, pl.UPW, H, hs2, static_cast<const float*>(saved), dctx, da, db, dc,
                      static_cast<float*>(ws));
 }
