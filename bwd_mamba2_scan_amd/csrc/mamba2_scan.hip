@@ -128,6 +128,11 @@ constexpr int kWriteThrough = 0x11;
 __device__ __forceinline__ void st4_through(__amdgpu_buffer_rsrc_t rs, unsigned off, v4f v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rs, off, 0, kWriteThrough);
 }
+// 16-byte store with the non-temporal hint (cache policy nt).
+constexpr int kNonTemporal = 0x2;
+__device__ __forceinline__ void st4_nt(__amdgpu_buffer_rsrc_t rs, unsigned off, v4f v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rs, off, 0, kNonTemporal);
+}
 __device__ __forceinline__ void st4_stream(float* p, v4f v) {
   __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
 }
@@ -196,10 +201,37 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   const int r1 = (t1 + kChunk - 1) / kChunk;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
   const int lane = tid & 63;
   const int kg = lane >> 4;  // k-group of the A/B operands, row quad of the result
   const int m = lane & 15;   // row of A (sample) / column of B and result (state)
+
+  // Scan lanes: waves 0..3, lane (i = lane>>4, n = lane&15) owns sample
+  // smp = 4*wave + i and state n.
+  const bool scanner = wave < 4;
+  const int smp = 4 * wave + kg;
+  const int pidx = plane_index(smp & 15, m);
+  // Saved planes of this (block, state group): alpha'_t and beta'_t for every
+  // step, x_K, then, when K spans several rounds, S_r for every round r.
+  const int nchunks = (K + kChunk - 1) / kChunk;  // rounds of the whole history
+  const size_t blk_stride = (size_t)saved_planes(K) * kPlane;
+  float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
+  float x = 0.f, c = 0.f;
+  // A chunked history (mode 2) starts from the state the carry pass left in
+  // the chunk's second S plane, and scales its S_r by the product of every
+  // later chunk's gates (the first S plane).  Read before anything is written.
+  // The loads are unconditional (from the x_K plane, which always exists,
+  // when not needed) and go out first, with the weight slab's: no wait on
+  // them is computed from a branch or holds the history stream back.
+  float suffix = 1.f;
+  {
+    const float x_in = sv[(size_t)(mode == 2 ? 2 * K + 2 + r0 : 2 * K) * kPlane + pidx];
+    const float s_in = sv[(size_t)(mode == 2 ? 2 * K + 1 + r0 : 2 * K) * kPlane + pidx];
+    const bool use = mode == 2 && scanner;
+    x = use ? x_in : 0.f;
+    suffix = use ? s_in : 1.f;
+  }
+  const float mstab = stab != nullptr ? stab[0] : 1.f;
 
   // (1) Weight slab, staged before any history load is issued: the slab's
   // loads would otherwise queue behind the CU's history stream and hold every
@@ -248,14 +280,14 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   if constexpr (PAIR) {
 #pragma unroll
     for (int r = 0; r < NCRP; ++r) {
-      const int pc = wave + kFwdWaves * r;
-      if (pc < NKC / 2) ld8_bf16(crow + pc * 32, hc[2 * r], hc[2 * r + 1]);
+      const int pc = min(wave + kFwdWaves * r, NKC / 2 - 1);
+      ld8_bf16(crow + pc * 32, hc[2 * r], hc[2 * r + 1]);
     }
   } else {
 #pragma unroll
     for (int r = 0; r < NCR; ++r) {
-      const int kc = wave + kFwdWaves * r;
-      if (kc < NKC) hc[r] = ld4_in(crow + kc * 16);
+      const int kc = min(wave + kFwdWaves * r, NKC - 1);
+      hc[r] = ld4_in(crow + kc * 16);
     }
   }
   const T* hbase = H + (size_t)smp_a * K * SH2 + koff;
@@ -267,71 +299,59 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     else
       hv[kc] = ld4_in(hbase + (size_t)t * SH2 + kc * 16);
   };
-  if (t0 + wave < t1) {
+  {
+    // a wave past the chunk's last step loads that step again (unused)
+    const int tf = min(t0 + wave, t1 - 1);
 #pragma unroll
-    for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(t0 + wave, kc);
+    for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(tf, kc);
   }
+  // keep these loads here, ahead of the readout (the compiler would
+  // otherwise sink them to their first use)
+  __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
-  // (3) readout partial over this wave's chunks
+  // (3) readout partial over this wave's chunks (a clamped chunk past the
+  // last one enters as zeros: no branch, so no load is moved under one)
   {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (PAIR) {
 #pragma unroll
       for (int r = 0; r < NCRP; ++r) {
         const int pc = wave + kFwdWaves * r;
-        if (pc < NKC / 2) {
+        const bool ok = pc < NKC / 2;
+        const int pcc = min(pc, NKC / 2 - 1);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const v4f bv = sWc[(2 * pc + h) * 64 + lane];
+        for (int h = 0; h < 2; ++h) {
+          const v4f bv = sWc[(2 * pcc + h) * 64 + lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc = mfma16x16x4(hc[2 * r + h][i], bv[i], acc);
-          }
+          for (int i = 0; i < 4; ++i) acc = mfma16x16x4(ok ? hc[2 * r + h][i] : 0.f, bv[i], acc);
         }
       }
     } else {
 #pragma unroll
       for (int r = 0; r < NCR; ++r) {
         const int kc = wave + kFwdWaves * r;
-        if (kc < NKC) {
-          const v4f bv = sWc[kc * 64 + lane];
-          acc = mfma16x16x4(hc[r][0], bv[0], acc);
-          acc = mfma16x16x4(hc[r][1], bv[1], acc);
-          acc = mfma16x16x4(hc[r][2], bv[2], acc);
-          acc = mfma16x16x4(hc[r][3], bv[3], acc);
-        }
+        const bool ok = kc < NKC;
+        const v4f bv = sWc[min(kc, NKC - 1) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mfma16x16x4(ok ? hc[r][i] : 0.f, bv[i], acc);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) sC[wave][(4 * kg + r) * kGroup + m] = acc[r];
   }
 
-  // Scan lanes: waves 0..3, lane (i = lane>>4, n = lane&15) owns sample
-  // smp = 4*wave + i and state n.
-  const bool scanner = wave < 4;
-  const int smp = 4 * wave + kg;
-  const int pidx = plane_index(smp & 15, m);
-  // Saved planes of this (block, state group): alpha'_t and beta'_t for every
-  // step, x_K, then, when K spans several rounds, S_r for every round r.
-  const int nchunks = (K + kChunk - 1) / kChunk;  // rounds of the whole history
-  const size_t blk_stride = (size_t)saved_planes(K) * kPlane;
-  float* sv = saved + ((size_t)blk * NG + sg) * blk_stride;
-  float x = 0.f, c = 0.f;
-  // A chunked history (mode 2) starts from the state the carry pass left in
-  // the chunk's second S plane, and scales its S_r by the product of every
-  // later chunk's gates (the first S plane).  Read before anything is written.
-  float suffix = 1.f;
-  if (mode == 2 && scanner) {
-    x = sv[(size_t)(2 * K + 2 + r0) * kPlane + pidx];
-    suffix = sv[(size_t)(2 * K + 1 + r0) * kPlane + pidx];
-  }
-  const float mstab = stab != nullptr ? stab[0] : 1.f;
-  float G[kChunk], U[kChunk];
+  float G[kChunk];
   float Gr[kRegRounds];  // gate product of each round (rounds >= kRegRounds park theirs in saved)
 #pragma unroll
   for (int i = 0; i < kRegRounds; ++i) Gr[i] = 1.f;
 
-  for (int ch = r0; ch < r1; ++ch) {
+  float gq[4] = {0.f, 0.f, 0.f, 0.f}, oq[4] = {0.f, 0.f, 0.f, 0.f};  // this wave's step: g, 1 - g
+  // Rounds r0 .. r1-1 of this chunk: at least one (a chunk is never empty),
+  // written as do-while so the first round's loads above stay where they
+  // are issued instead of moving into a loop-entry test.
+  int ch = r0;
+  do {
     const int lr = ch - r0;  // round within this chunk
     const int t = ch * kChunk + wave;
     if (t < t1) {
@@ -360,9 +380,21 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
         for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(t + kChunk, kc);
       }
       __builtin_amdgcn_sched_barrier(0);
+      // The gates of this step, for this lane's four samples (rows 4kg+r):
+      // sigmoid(a) = 1 / (1 + e^-a) from the hardware exp2 and reciprocal
+      // (each within ~1 ulp); e = inf gives g = 0, never NaN.  1 - g is
+      // computed without cancellation: e*g = e/(1+e) for a > 0.  The
+      // stability multiplier m scales the gate and its derivative (m = 1
+      // leaves every product bit-identical).  The exchange carries m*g and b;
+      // g and 1-g stay here for this step's alpha' below.
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sXa[wave][(4 * kg + r) * kGroup + m] = acca[r];
+        const float a = acca[r];
+        const float e = __expf(-a);
+        const float g = __builtin_amdgcn_rcpf(1.f + e);
+        gq[r] = g;
+        oq[r] = a > 0.f ? e * g : 1.f - g;
+        sXa[wave][(4 * kg + r) * kGroup + m] = g * mstab;
         sXb[wave][(4 * kg + r) * kGroup + m] = accb[r];
       }
     }
@@ -377,38 +409,27 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
         c = s;
       }
       const int tn = min(kChunk, t1 - ch * kChunk);
+      // The recurrence; each step's slot then holds the state it started
+      // from (x_t), for the projecting wave's alpha'.
 #pragma unroll
       for (int tt = 0; tt < kChunk; ++tt) {
         if (tt < tn) {
-          const float a = sXa[tt][idx];
+          G[tt] = sXa[tt][idx];
           const float b = sXb[tt][idx];
-          // sigmoid(a) = 1 / (1 + e^-a) from the hardware exp2 and reciprocal
-          // (each within ~1 ulp); e = inf gives g = 0, never NaN.
-          const float e = __expf(-a);
-          const float g = __builtin_amdgcn_rcpf(1.f + e);
-          // 1 - g, computed without cancellation: e*g = e/(1+e) for a > 0.
-          const float omg = a > 0.f ? e * g : 1.f - g;
-          // stability multiplier m scales the gate and its derivative (m = 1
-          // leaves every product bit-identical)
-          U[tt] = x * g * omg * mstab;
-          G[tt] = g * mstab;
+          sXa[tt][idx] = x;
           x = G[tt] * x + b;
         }
       }
       // Round-local reverse pass: beta'_t = c * prod of this round's later
-      // gates, alpha'_t = beta'_t * u_t.  The full terms are
-      // beta_t = S_r beta'_t and alpha_t = S_r alpha'_t with S_r the product
-      // of every gate of the later rounds; the backward applies S_r.
-      // (the summary pass of a chunked history keeps only the gate products)
+      // gates (into the step's second slot), and the round's gate product.
+      // The full terms are beta_t = S_r beta'_t and alpha_t = S_r alpha'_t
+      // with S_r the product of every gate of the later rounds; the backward
+      // applies S_r.
       float P = c, gp = 1.f;
 #pragma unroll
       for (int tt = kChunk - 1; tt >= 0; --tt) {
         if (tt < tn) {
-          const int tg = ch * kChunk + tt;
-          if (mode != 1) {
-            st_stream(&sv[(size_t)(2 * tg) * kPlane + pidx], P * U[tt]);
-            st_stream(&sv[(size_t)(2 * tg + 1) * kPlane + pidx], P);
-          }
+          sXb[tt][idx] = P;
           P *= G[tt];
           gp *= G[tt];
         }
@@ -424,7 +445,32 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
       }
     }
     __syncthreads();
-  }
+    // Each projecting wave writes its step's planes: beta'_t and
+    // alpha'_t = beta'_t * x_t * m g (1 - g), one float4 per lane (its four
+    // samples 4kg+r at state m are entries kg*64 + 4m + r of a plane).  The
+    // stores are unconditional; a descriptor of size 0 drops them for a wave
+    // past the chunk's last step and in the summary pass, so no memory
+    // operation sits under a branch while the next round's loads are in
+    // flight.  (Every wave reads back only its own slots here, and writes
+    // them again only after its next projection, so no barrier is needed.)
+    {
+      const bool st_ok = t < t1 && mode != 1;
+      const int ts = min(t, t1 - 1);
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(sv + (size_t)(2 * ts) * kPlane, st_ok ? 2 * kPlane * sizeof(float) : 0u);
+      v4f al, be;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float xv = sXa[wave][(4 * kg + r) * kGroup + m];
+        const float Pv = sXb[wave][(4 * kg + r) * kGroup + m];
+        al[r] = Pv * (xv * gq[r] * oq[r] * mstab);
+        be[r] = Pv;
+      }
+      const unsigned off = (unsigned)((kg * 64 + 4 * m) * sizeof(float));
+      st4_nt(rs, off, al);
+      st4_nt(rs, off + kPlane * sizeof(float), be);
+    }
+  } while (++ch < r1);
 
   if (!scanner) return;
 
