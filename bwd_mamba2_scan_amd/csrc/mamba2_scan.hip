@@ -780,9 +780,18 @@ __device__ __forceinline__ v4f reduce_slices(const float* __restrict__ src, size
   const int p0 = grp * pc;
   const int p1 = min(P, p0 + pc);
   v4f s = {0.f, 0.f, 0.f, 0.f};
-  if (ok) {
-#pragma unroll 4
-    for (int pp = p0; pp < p1; ++pp) s += ld4(src + (size_t)pp * stride);
+  // Eight loads in flight per pass, all unconditional (clamped to a valid
+  // slice); a load past the group's slices, or of a thread with no output,
+  // is not added.  The sum runs over p0 .. p1-1 in order.
+  for (int b = p0; b < p0 + pc; b += 8) {
+    v4f v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ld4(src + (size_t)min(b + j, P - 1) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const v4f t = s + v[j];
+      s = (ok && b + j < p1) ? t : s;
+    }
   }
   sPart[grp][ql] = s;
   __syncthreads();
