@@ -950,12 +950,13 @@ __global__ __launch_bounds__(kBlendWaves * 64) void blend_bwd_kernel(
 //   d_h_s2[b][j]         = sum_s d_c[b,s]   W_C[j][s]
 // with d_a, d_b, d_c formed from `saved` and d_context exactly as in the
 // backward.  Neither h_history nor h_s2 is read.
-//   grid = 8 * (SH2/64) * ceil(NCH / 8), 256 threads.  Work-group: a chunk of
-//   BPW consecutive 16-sample blocks and one 64-feature column block; the
-//   column blocks of a chunk run on one XCD so they share the saved planes
-//   in L2.  A unit is (sample block, step t) for t < K, or the readout
-//   (t = K); wave w takes units w, w+4, ... of its work-group and requests
-//   the next unit's operands while it multiplies the current one.
+//   grid = 8 * (SH2/64) * ceil(NSL / 8), 256 threads.  A unit is (sample
+//   block, step t) for t < K, or the readout (t = K), numbered block-major;
+//   work-group: a slice of UPW consecutive units (so few samples with a long
+//   history still spread over ~1024 work-groups) and one 64-feature column
+//   block; the column blocks of a slice run on one XCD so they share the
+//   saved planes in L2.  Wave w takes units w, w+4, ... of its slice and
+//   requests the next unit's operands while it multiplies the current one.
 // Operands: a unit's saved planes and the block's d_context arrive as whole
 // 1 KiB rows (one 16-byte load per lane each, four per unit at D = 16) and
 // pass through the wave's LDS tile into the MFMA layout.  The kernel writes
@@ -991,7 +992,7 @@ struct DinUnit {
 };
 
 struct DinCtx {
-  int B, K, blk0;
+  int B, K, u0;  // u0: the work-group's first unit (units are (block, t), t-minor)
   size_t blk_stride;
   const float* saved;
   const float* dctx;
@@ -1001,9 +1002,8 @@ template <int NGT, bool ROUNDS>
 __device__ __forceinline__ void din_load(DinUnit<NGT>& U, int u, const DinCtx& c, int lane) {
   constexpr int D = NGT * kGroup;
   const int KU = c.K + 1;
-  const int bi = u / KU;
-  const int t = u - bi * KU;
-  const int blk = c.blk0 + bi;
+  const int blk = (c.u0 + u) / KU;
+  const int t = c.u0 + u - blk * KU;
   const bool step = t < c.K;
   const int p0 = step ? 2 * t : 2 * c.K;
   const int p1 = step ? 2 * t + 1 : 2 * c.K;
@@ -1057,9 +1057,8 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
   constexpr int D = NGT * kGroup;
   constexpr int NQ = D / 4;
   const int KU = c.K + 1;
-  const int bi = u / KU;
-  const int t = u - bi * KU;
-  const int blk = c.blk0 + bi;
+  const int blk = (c.u0 + u) / KU;
+  const int t = c.u0 + u - blk * KU;
   const bool readout = t == c.K;
 
   // operands into the tile: [kind][group] planes, then the d_context rows
@@ -1148,7 +1147,7 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
 
 template <int NGT, bool ROUNDS>
 __global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
-    int B, int K, int SH2, int NB, int BPW,
+    int B, int K, int SH2, int NB, int UPW,
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
     const float* __restrict__ saved, const float* __restrict__ dctx,
     float* __restrict__ dH, float* __restrict__ dhs2) {
@@ -1162,16 +1161,17 @@ __global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
   const int xcd = blockIdx.x & 7;
   const int round = blockIdx.x >> 3;
   const int jb = round % NJB;
-  const int chunk = (round / NJB) * 8 + xcd;
+  const int slice = (round / NJB) * 8 + xcd;
+  const int total = NB * (K + 1);
   DinCtx c;
-  c.blk0 = chunk * BPW;
-  if (c.blk0 >= NB) return;
+  c.u0 = slice * UPW;
+  if (c.u0 >= total) return;
   c.B = B;
   c.K = K;
   c.blk_stride = (size_t)saved_planes(K) * kPlane;
   c.saved = saved;
   c.dctx = dctx;
-  const int n_units = min(BPW, NB - c.blk0) * (K + 1);
+  const int n_units = min(UPW, total - c.u0);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1383,25 +1383,30 @@ size_t blend_ws_bytes(const Plan& pl) {
 }
 
 // Chunk size: about kDinTargetWGs work-groups over all chunks and column blocks.
-int dinput_bpw(const Plan& pl) {
-  const long long units = (long long)pl.NB * pl.NJB * (pl.K + 1);
-  const long long per_wg = (units + kDinTargetWGs - 1) / kDinTargetWGs;
-  long long bpw = (per_wg + pl.K) / (pl.K + 1);
-  return (int)(bpw < 1 ? 1 : (bpw > pl.NB ? pl.NB : bpw));
+// Units per work-group: the (block, t) units of all blocks, in order, split
+// into slices so that about kDinTargetWGs work-groups run (at least one unit
+// per wave), whatever the mix of samples and history length.
+int dinput_upw(const Plan& pl) {
+  const long long units = (long long)pl.NB * (pl.K + 1);
+  const long long slices = (kDinTargetWGs + pl.NJB - 1) / pl.NJB;
+  long long upw = (units + slices - 1) / slices;
+  if (upw < kDinWaves) upw = kDinWaves;
+  return (int)(upw > units ? units : upw);
 }
 
 template <int NGT>
 void launch_dinput(const Plan& pl, const float* WA, const float* WB, const float* WC, const float* sv,
                    const float* dctx, float* dH, float* dhs2, hipStream_t st) {
-  const int bpw = dinput_bpw(pl);
-  const int nch = (pl.NB + bpw - 1) / bpw;
-  const int grid = 8 * pl.NJB * ((nch + 7) / 8);
+  const int upw = dinput_upw(pl);
+  const long long units = (long long)pl.NB * (pl.K + 1);
+  const int nsl = (int)((units + upw - 1) / upw);
+  const int grid = 8 * pl.NJB * ((nsl + 7) / 8);
   if (pl.K > kChunk)
     hipLaunchKernelGGL((dinput_kernel<NGT, true>), dim3(grid), dim3(kDinWaves * 64), 0, st, pl.B, pl.K, pl.SH2,
-                       pl.NB, bpw, WA, WB, WC, sv, dctx, dH, dhs2);
+                       pl.NB, upw, WA, WB, WC, sv, dctx, dH, dhs2);
   else
     hipLaunchKernelGGL((dinput_kernel<NGT, false>), dim3(grid), dim3(kDinWaves * 64), 0, st, pl.B, pl.K, pl.SH2,
-                       pl.NB, bpw, WA, WB, WC, sv, dctx, dH, dhs2);
+                       pl.NB, upw, WA, WB, WC, sv, dctx, dH, dhs2);
 }
 
 }  // namespace

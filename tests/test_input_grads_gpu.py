@@ -15,7 +15,7 @@ import torch
 import bwd_mamba2_scan_amd as m2
 from oracle import mamba2_oracle as orc
 from tests.inputs import make_inputs, workload_inputs
-from tests.test_parity_gpu import EDGE_SHAPES, _to_dev, assert_elementwise
+from tests.test_parity_gpu import EDGE_SHAPES, LONG_FEW_SHAPES, _to_dev, assert_elementwise
 
 pytestmark = pytest.mark.gpu
 
@@ -54,15 +54,28 @@ def test_input_grads_workloads(name):
     assert_elementwise(dhs2.cpu().numpy(), ref.d_h_s2, "d_h_s2")
 
 
-@pytest.mark.parametrize("name", ["long_history", "wide_state"])
+@pytest.mark.parametrize("B,K,SH2,D", LONG_FEW_SHAPES, ids=lambda v: str(v))
+def test_input_grads_long_few(B, K, SH2, D):
+    """Few samples, long histories: unit slices that start and end inside a block."""
+    inputs = make_inputs(B, K, SH2, D, seed=B + K + 3, gate_bias=2.0)
+    dH, dhs2, _ = gpu_input_grads(_to_dev(inputs), K)
+    ref = oracle_input_grads(inputs)
+    assert_elementwise(dH.cpu().numpy(), ref.d_h_history, "d_h_history")
+    assert_elementwise(dhs2.cpu().numpy(), ref.d_h_s2, "d_h_s2")
+
+
+@pytest.mark.parametrize("name", ["long_history", "wide_state", "long_few"])
 def test_input_grads_large_sampled(name):
-    """Full-size launch; 512 sampled samples (both ends, the middle, random) checked."""
+    """Full-size launch; up to 512 samples (both ends, the middle, random) checked."""
     inputs = workload_inputs(name)
     B, K = inputs["h_history"].shape[:2]
     dH, dhs2, _ = gpu_input_grads(_to_dev(inputs), K)
     rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([np.arange(16), np.arange(B - 16, B), B // 2 + np.arange(16),
-                                     rng.choice(B, 464, replace=False)]))
+    if B <= 512:
+        rows = np.arange(B)
+    else:
+        rows = np.unique(np.concatenate([np.arange(16), np.arange(B - 16, B), B // 2 + np.arange(16),
+                                         rng.choice(B, 464, replace=False)]))
     ref = oracle_input_grads(inputs, rows)
     idx = torch.from_numpy(rows).to(dH.device)
     assert_elementwise(dH.index_select(0, idx).cpu().numpy(), ref.d_h_history, "d_h_history")
