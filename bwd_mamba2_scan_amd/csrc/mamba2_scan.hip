@@ -57,6 +57,12 @@ constexpr int kPlane = kBlock * kGroup;  // floats in one (sample, state) plane
 constexpr int kColBlock = 64;    // trunk features per backward column block
 constexpr int kFwdWaves = 8;
 constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
+// Sample blocks per forward work-group: two when the weight slab is so large
+// (SH2 >= 320) that two one-block work-groups would not fit a CU's LDS, so a
+// CU still runs sixteen forward waves; one otherwise (two work-groups per
+// CU, which measured faster there).
+__host__ __device__ constexpr int fwd_blocks(int nkc) { return nkc >= 20 ? 2 : 1; }
+__host__ __device__ constexpr int fwd_threads(int nkc) { return fwd_blocks(nkc) * kFwdWaves * 64; }
 constexpr int kFwdPrefetch = 6;    // history loads each forward wave keeps in flight
 constexpr int kRegRounds = 8;      // rounds whose gate product the forward keeps in registers
 constexpr int kFwdChunkTarget = 512;  // forward work-groups a chunked history aims for
@@ -162,13 +168,15 @@ __host__ __device__ __forceinline__ int saved_planes(int K) {
 // saturate HBM without queueing so deep that the first data arrives late.
 // The first loads of round r+1 go out before the scan of round r.
 template <int NKC, class T>  // SH2 / 16 trunk chunks; T = fp32 or bf16 trunk inputs
-__global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
+__global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     int B, int K, int NG, int NB,
     const T* __restrict__ H, const T* __restrict__ hs2,
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
     const float* __restrict__ stab, float* __restrict__ ctx, float* __restrict__ saved,
     int L, int C, int mode) {
   constexpr int SH2 = NKC * 16;
+  constexpr int kFwdBlocks = fwd_blocks(NKC);
+  constexpr int kFwdThreads = fwd_threads(NKC);
   constexpr int NCR = (NKC + kFwdWaves - 1) / kFwdWaves;                   // readout chunks per wave
   constexpr int NCRP = (NKC / 2 + kFwdWaves - 1) / kFwdWaves;              // readout pairs per wave (bf16)
   // bf16 inputs load in pairs of chunks: lane (kg, m) takes features
@@ -183,17 +191,17 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   __shared__ v4f sWa[NKC * 64];
   __shared__ v4f sWb[NKC * 64];
   __shared__ v4f sWc[NKC * 64];
-  __shared__ float sXa[kChunk][kPlane];
-  __shared__ float sXb[kChunk][kPlane];
-  __shared__ float sC[kFwdWaves][kPlane];
+  __shared__ float sXa[kFwdBlocks][kChunk][kPlane];
+  __shared__ float sXb[kFwdBlocks][kChunk][kPlane];
+  __shared__ float sC[kFwdBlocks][kFwdWaves][kPlane];
 
   const int D = NG * kGroup;
   const int xcd = blockIdx.x & 7;
   const int round = blockIdx.x >> 3;
   const int sg = round % NG;
   const int cidx = (round / NG) % C;  // history chunk of this work-group (C = 1: the whole history)
-  const int blk = (round / NG / C) * 8 + xcd;
-  if (blk >= NB) return;
+  const int pair = (round / NG / C) * 8 + xcd;  // this work-group's sample blocks
+  if (pair * kFwdBlocks >= NB) return;
   // steps [t0, t1) of this chunk: rounds r0 .. r1-1 (a round is kChunk steps)
   const int t0 = cidx * L;
   const int t1 = cidx == C - 1 ? K : t0 + L;
@@ -201,14 +209,20 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   const int r1 = (t1 + kChunk - 1) / kChunk;
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
+  const int wg_wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
+  const int half = wg_wave / kFwdWaves;  // which of the work-group's blocks this wave serves
+  const int wave = wg_wave % kFwdWaves;  // wave within its block
   const int lane = tid & 63;
+  // The second block of the last pair may lie past NB: its waves take part
+  // in every barrier but load a valid block (clamped) and store nothing.
+  const bool blk_ok = pair * kFwdBlocks + half < NB;
+  const int blk = min(pair * kFwdBlocks + half, NB - 1);
   const int kg = lane >> 4;  // k-group of the A/B operands, row quad of the result
   const int m = lane & 15;   // row of A (sample) / column of B and result (state)
 
   // Scan lanes: waves 0..3, lane (i = lane>>4, n = lane&15) owns sample
   // smp = 4*wave + i and state n.
-  const bool scanner = wave < 4;
+  const bool scanner = wave < 4 && blk_ok;
   const int smp = 4 * wave + kg;
   const int pidx = plane_index(smp & 15, m);
   // Saved planes of this (block, state group): alpha'_t and beta'_t for every
@@ -240,11 +254,11 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
   // W[kc*16 + 4*(l>>4) + i][sg*16 + (l&15)] for i = 0..3.
   {
     constexpr int NW4 = SH2 * 4;  // float4s per matrix slab
-    constexpr int NWT = (3 * NW4 + kFwdWaves * 64 - 1) / (kFwdWaves * 64);
+    constexpr int NWT = (3 * NW4 + kFwdThreads - 1) / kFwdThreads;
     v4f wr[NWT];
 #pragma unroll
     for (int it = 0; it < NWT; ++it) {
-      const int f = tid + it * kFwdWaves * 64;
+      const int f = tid + it * kFwdThreads;
       if (f < 3 * NW4) {
         const int mat = f / NW4, r = f - mat * NW4;
         const float* W = mat == 0 ? WA : (mat == 1 ? WB : WC);
@@ -253,7 +267,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     }
 #pragma unroll
     for (int it = 0; it < NWT; ++it) {
-      const int f = tid + it * kFwdWaves * 64;
+      const int f = tid + it * kFwdThreads;
       if (f < 3 * NW4) {
         const int mat = f / NW4, r = f - mat * NW4;
         const int j = r >> 2, s4 = r & 3;
@@ -338,7 +352,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
       }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sC[wave][(4 * kg + r) * kGroup + m] = acc[r];
+    for (int r = 0; r < 4; ++r) sC[half][wave][(4 * kg + r) * kGroup + m] = acc[r];
   }
 
   float G[kChunk];
@@ -394,8 +408,8 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
         const float g = __builtin_amdgcn_rcpf(1.f + e);
         gq[r] = g;
         oq[r] = a > 0.f ? e * g : 1.f - g;
-        sXa[wave][(4 * kg + r) * kGroup + m] = g * mstab;
-        sXb[wave][(4 * kg + r) * kGroup + m] = accb[r];
+        sXa[half][wave][(4 * kg + r) * kGroup + m] = g * mstab;
+        sXb[half][wave][(4 * kg + r) * kGroup + m] = accb[r];
       }
     }
     __syncthreads();
@@ -405,7 +419,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
       if (ch == r0) {
         float s = 0.f;
 #pragma unroll
-        for (int w = 0; w < kFwdWaves; ++w) s += sC[w][idx];
+        for (int w = 0; w < kFwdWaves; ++w) s += sC[half][w][idx];
         c = s;
       }
       const int tn = min(kChunk, t1 - ch * kChunk);
@@ -414,9 +428,9 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
 #pragma unroll
       for (int tt = 0; tt < kChunk; ++tt) {
         if (tt < tn) {
-          G[tt] = sXa[tt][idx];
-          const float b = sXb[tt][idx];
-          sXa[tt][idx] = x;
+          G[tt] = sXa[half][tt][idx];
+          const float b = sXb[half][tt][idx];
+          sXa[half][tt][idx] = x;
           x = G[tt] * x + b;
         }
       }
@@ -429,7 +443,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
 #pragma unroll
       for (int tt = kChunk - 1; tt >= 0; --tt) {
         if (tt < tn) {
-          sXb[tt][idx] = P;
+          sXb[half][tt][idx] = P;
           P *= G[tt];
           gp *= G[tt];
         }
@@ -454,15 +468,15 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(
     // flight.  (Every wave reads back only its own slots here, and writes
     // them again only after its next projection, so no barrier is needed.)
     {
-      const bool st_ok = t < t1 && mode != 1;
+      const bool st_ok = t < t1 && mode != 1 && blk_ok;
       const int ts = min(t, t1 - 1);
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(sv + (size_t)(2 * ts) * kPlane, st_ok ? 2 * kPlane * sizeof(float) : 0u);
       v4f al, be;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float xv = sXa[wave][(4 * kg + r) * kGroup + m];
-        const float Pv = sXb[wave][(4 * kg + r) * kGroup + m];
+        const float xv = sXa[half][wave][(4 * kg + r) * kGroup + m];
+        const float Pv = sXb[half][wave][(4 * kg + r) * kGroup + m];
         al[r] = Pv * (xv * gq[r] * oq[r] * mstab);
         be[r] = Pv;
       }
@@ -1284,16 +1298,19 @@ void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const
                 const float* WC, const float* stab, float* ctx, float* saved, hipStream_t st) {
   int L, C;
   fwd_chunks(pl, &L, &C);
-  const int grid = 8 * pl.NG * C * ((pl.NB + 7) / 8);
+  constexpr int kFwdBlocks = fwd_blocks(NKC);
+  constexpr int kFwdThreads = fwd_threads(NKC);
+  const int pairs = (pl.NB + kFwdBlocks - 1) / kFwdBlocks;
+  const int grid = 8 * pl.NG * C * ((pairs + 7) / 8);
   if (C == 1) {
-    hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB,
+    hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
                        H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 0);
     return;
   }
-  hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
+  hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
                      hs2, WA, WB, WC, stab, ctx, saved, L, C, 1);
   hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG), dim3(kPlane), 0, st, pl.NB * pl.NG, pl.K, L, C, saved);
-  hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
+  hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
                      hs2, WA, WB, WC, stab, ctx, saved, L, C, 2);
 }
 
