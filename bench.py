@@ -114,7 +114,7 @@ def cpu_baseline(workload_name, budget_s=12.0):
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s or len(times) >= 1000:
             break
-    return {
+    out = {
         "value": round(statistics.median(times) * 1e3, 3),
         "unit": "ms",
         "cores": cores,
@@ -122,6 +122,23 @@ def cpu_baseline(workload_name, budget_s=12.0):
         "sample": f"full {workload_name} batch (fp64 numpy oracle fwd+bwd), median of {len(times)} runs "
                   f"in {time.perf_counter() - t_start:.1f} s",
     }
+    # the same on one thread (BLAS limited to 1), a shorter sample
+    try:
+        from threadpoolctl import threadpool_limits
+        one = []
+        t1 = time.perf_counter()
+        with threadpool_limits(limits=1):
+            while True:
+                t0 = time.perf_counter()
+                orc.fwd_bwd(inp)
+                one.append(time.perf_counter() - t0)
+                if time.perf_counter() - t1 > budget_s / 2 or len(one) >= 200:
+                    break
+        out["single_thread"] = {"value": round(statistics.median(one) * 1e3, 3), "unit": "ms", "cores": 1,
+                                "sample": f"median of {len(one)} runs"}
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    return out
 
 
 def parity_gate(m2, torch, t, inputs):
