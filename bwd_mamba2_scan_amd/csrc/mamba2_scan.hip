@@ -167,7 +167,10 @@ __host__ __device__ __forceinline__ int saved_planes(int K) {
 // min(kFwdPrefetch, SH2/16) history loads in flight: enough in total to
 // saturate HBM without queueing so deep that the first data arrives late.
 // The first loads of round r+1 go out before the scan of round r.
-template <int NKC, class T>  // SH2 / 16 trunk chunks; T = fp32 or bf16 trunk inputs
+// REPLAY (the second pass of a chunked history): the step projections a, b
+// come from the alpha'/beta' slots, where the summary pass left them, instead
+// of from h_history; only W_C is staged, for the readout.
+template <int NKC, class T, bool REPLAY = false>  // SH2 / 16 trunk chunks; T = fp32 or bf16 trunk inputs
 __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     int B, int K, int NG, int NB,
     const T* __restrict__ H, const T* __restrict__ hs2,
@@ -254,13 +257,15 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // W[kc*16 + 4*(l>>4) + i][sg*16 + (l&15)] for i = 0..3.
   {
     constexpr int NW4 = SH2 * 4;  // float4s per matrix slab
-    constexpr int NWT = (3 * NW4 + kFwdThreads - 1) / kFwdThreads;
+    constexpr int NMAT = REPLAY ? 1 : 3;  // REPLAY: W_C only
+    constexpr int M0 = 3 - NMAT;
+    constexpr int NWT = (NMAT * NW4 + kFwdThreads - 1) / kFwdThreads;
     v4f wr[NWT];
 #pragma unroll
     for (int it = 0; it < NWT; ++it) {
       const int f = tid + it * kFwdThreads;
-      if (f < 3 * NW4) {
-        const int mat = f / NW4, r = f - mat * NW4;
+      if (f < NMAT * NW4) {
+        const int mat = M0 + f / NW4, r = f - (mat - M0) * NW4;
         const float* W = mat == 0 ? WA : (mat == 1 ? WB : WC);
         wr[it] = ld4(W + (size_t)(r >> 2) * D + sg * kGroup + 4 * (r & 3));
       }
@@ -268,8 +273,8 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 #pragma unroll
     for (int it = 0; it < NWT; ++it) {
       const int f = tid + it * kFwdThreads;
-      if (f < 3 * NW4) {
-        const int mat = f / NW4, r = f - mat * NW4;
+      if (f < NMAT * NW4) {
+        const int mat = M0 + f / NW4, r = f - (mat - M0) * NW4;
         const int j = r >> 2, s4 = r & 3;
         float* dst = reinterpret_cast<float*>(mat == 0 ? sWa : (mat == 1 ? sWb : sWc));
         // feature j -> (chunk, k-group, element) of the A/B operand order
@@ -313,11 +318,21 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     else
       hv[kc] = ld4_in(hbase + (size_t)t * SH2 + kc * 16);
   };
+  // REPLAY: this wave's step projections, as float4s of the alpha'/beta'
+  // slots (its four samples 4kg+r at state m are entries kg*64 + 4m + r,
+  // the MFMA result layout)
+  const int toff = kg * 64 + 4 * m;
+  v4f pa = {0.f, 0.f, 0.f, 0.f}, pb = {0.f, 0.f, 0.f, 0.f};
   {
     // a wave past the chunk's last step loads that step again (unused)
     const int tf = min(t0 + wave, t1 - 1);
+    if constexpr (REPLAY) {
+      pa = ld4(sv + (size_t)(2 * tf) * kPlane + toff);
+      pb = ld4(sv + (size_t)(2 * tf + 1) * kPlane + toff);
+    } else {
 #pragma unroll
-    for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(tf, kc);
+      for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(tf, kc);
+    }
   }
   // keep these loads here, ahead of the readout (the compiler would
   // otherwise sink them to their first use)
@@ -368,9 +383,19 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   do {
     const int lr = ch - r0;  // round within this chunk
     const int t = ch * kChunk + wave;
+    v4f sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};  // this step's projections
     if (t < t1) {
       v4f acca = {0.f, 0.f, 0.f, 0.f};
       v4f accb = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (REPLAY) {
+        acca = pa;
+        accb = pb;
+        // the next round's projections go out now
+        if (t + kChunk < t1) {
+          pa = ld4(sv + (size_t)(2 * (t + kChunk)) * kPlane + toff);
+          pb = ld4(sv + (size_t)(2 * (t + kChunk) + 1) * kPlane + toff);
+        }
+      } else {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         const v4f wa = sWa[kc * 64 + lane];
@@ -393,6 +418,9 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 #pragma unroll
         for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(t + kChunk, kc);
       }
+      }
+      sa = acca;
+      sb = accb;
       __builtin_amdgcn_sched_barrier(0);
       // The gates of this step, for this lane's four samples (rows 4kg+r):
       // sigmoid(a) = 1 / (1 + e^-a) from the hardware exp2 and reciprocal
@@ -461,14 +489,16 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     __syncthreads();
     // Each projecting wave writes its step's planes: beta'_t and
     // alpha'_t = beta'_t * x_t * m g (1 - g), one float4 per lane (its four
-    // samples 4kg+r at state m are entries kg*64 + 4m + r of a plane).  The
-    // stores are unconditional; a descriptor of size 0 drops them for a wave
-    // past the chunk's last step and in the summary pass, so no memory
-    // operation sits under a branch while the next round's loads are in
-    // flight.  (Every wave reads back only its own slots here, and writes
-    // them again only after its next projection, so no barrier is needed.)
+    // samples 4kg+r at state m are entries kg*64 + 4m + r of a plane); the
+    // summary pass of a chunked history writes the projections a_t and b_t
+    // there instead, for the second pass to replay.  The stores are
+    // unconditional; a descriptor of size 0 drops them for a wave past the
+    // chunk's last step, so no memory operation sits under a branch while the
+    // next round's loads are in flight.  (Every wave reads back only its own
+    // slots here, and writes them again only after its next projection, so
+    // no barrier is needed.)
     {
-      const bool st_ok = t < t1 && mode != 1 && blk_ok;
+      const bool st_ok = t < t1 && blk_ok;
       const int ts = min(t, t1 - 1);
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(sv + (size_t)(2 * ts) * kPlane, st_ok ? 2 * kPlane * sizeof(float) : 0u);
@@ -480,9 +510,9 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
         al[r] = Pv * (xv * gq[r] * oq[r] * mstab);
         be[r] = Pv;
       }
-      const unsigned off = (unsigned)((kg * 64 + 4 * m) * sizeof(float));
-      st4_nt(rs, off, al);
-      st4_nt(rs, off + kPlane * sizeof(float), be);
+      const unsigned off = (unsigned)(toff * sizeof(float));
+      st4_nt(rs, off, mode == 1 ? sa : al);
+      st4_nt(rs, off + kPlane * sizeof(float), mode == 1 ? sb : be);
     }
   } while (++ch < r1);
 
@@ -1310,8 +1340,8 @@ void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const
   hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
                      hs2, WA, WB, WC, stab, ctx, saved, L, C, 1);
   hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG), dim3(kPlane), 0, st, pl.NB * pl.NG, pl.K, L, C, saved);
-  hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
-                     hs2, WA, WB, WC, stab, ctx, saved, L, C, 2);
+  hipLaunchKernelGGL((fwd_kernel<NKC, T, true>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
+                     H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 2);
 }
 
 int check_bwd_common(const Plan& pl, const void* H, const void* hs2, const void* saved, size_t saved_bytes,
