@@ -101,6 +101,7 @@ __device__ __forceinline__ v4f ld4_in<float>(const float* p) {
 // Eight consecutive bf16 values as one 16-byte streamed load, widened into
 // two groups of four.
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void ld8_bf16(const bf16_t* p, v4f& lo, v4f& hi) {
   const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
   lo[0] = __uint_as_float(w[0] << 16);
@@ -191,12 +192,23 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 #endif
   constexpr int PFP = PAIR ? (FWD_PAIR_PF < NKC / 2 ? FWD_PAIR_PF : NKC / 2) : 0;  // pairs in flight
   constexpr int PF = PAIR ? 2 * PFP : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC);   // chunks in flight
-  __shared__ v4f sWa[NKC * 64];
-  __shared__ v4f sWb[NKC * 64];
+  // bf16 trunk inputs feed bf16 MFMAs directly: each weight is split
+  // exactly into three bf16 terms (hi + mid + lo == W for every fp32 W above
+  // ~1e-33), so every product is exact and only the fp32 accumulation
+  // rounds, as with fp32 MFMAs.  The readout keeps fp32 MFMAs on widened
+  // h_s2.
+  constexpr bool BFM = PAIR && !REPLAY;
+  constexpr int NP = NKC / 2;  // 32-feature pairs of chunks
+  __shared__ v4f sWa[BFM ? 1 : NKC * 64];
+  __shared__ v4f sWb[BFM ? 1 : NKC * 64];
+  __shared__ v4u sWab[BFM ? 6 * NP * 64 : 1];  // [mat A|B][term hi|mid|lo][pair][lane]: 8 bf16
   __shared__ v4f sWc[NKC * 64];
   __shared__ float sXa[kFwdBlocks][kChunk][kPlane];
   __shared__ float sXb[kFwdBlocks][kChunk][kPlane];
-  __shared__ float sC[kFwdBlocks][kFwdWaves][kPlane];
+  // readout partials; with BFM they share sXa's memory (summed into c
+  // before the first exchange writes it), which keeps two work-groups per CU
+  __shared__ float sCbuf[BFM ? 1 : kFwdBlocks * kFwdWaves * kPlane];
+  float(*sC)[kFwdWaves][kPlane] = BFM ? sXa : reinterpret_cast<float(*)[kFwdWaves][kPlane]>(sCbuf);
 
   const int D = NG * kGroup;
   const int xcd = blockIdx.x & 7;
@@ -255,7 +267,64 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // MFMA back.  Each thread loads rows of W_X[j][sg*16 + 4*s4 .. +3] as float4
   // and scatters them into the B-operand layout, where entry (kc, l) holds
   // W[kc*16 + 4*(l>>4) + i][sg*16 + (l&15)] for i = 0..3.
-  {
+  if constexpr (BFM) {
+    // W_A, W_B: a task is (matrix, octet o of rows 8o..8o+7, states
+    // 4*s4..4*s4+3); per state n it writes the eight rows' three terms as
+    // three 16-byte entries (pair o/4, lane (o%4, n)).  W_C as for fp32.
+    constexpr int NTASK = 2 * (SH2 / 8) * 4;  // = SH2 <= half the threads
+    static_assert(2 * NTASK <= kFwdThreads, "one task per thread");
+    if (tid < NTASK) {
+      const int task = tid;
+      const int mat = task / ((SH2 / 8) * 4);
+      const int o = (task >> 2) % (SH2 / 8);
+      const int s4 = task & 3;
+      const float* W = mat == 0 ? WA : WB;
+      v4f w[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) w[jj] = ld4(W + (size_t)(8 * o + jj) * D + sg * kGroup + 4 * s4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v8bf th, tm, tl;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float v = w[jj][q];
+          const __bf16 hi = (__bf16)v;
+          const float r1 = v - (float)hi;
+          const __bf16 mi = (__bf16)r1;
+          const float r2 = r1 - (float)mi;
+          th[jj] = hi;
+          tm[jj] = mi;
+          tl[jj] = (__bf16)r2;
+        }
+        const int e = ((o >> 2) * 64 + (o & 3) * 16 + 4 * s4 + q);
+        sWab[(mat * 3 + 0) * NP * 64 + e] = __builtin_bit_cast(v4u, th);
+        sWab[(mat * 3 + 1) * NP * 64 + e] = __builtin_bit_cast(v4u, tm);
+        sWab[(mat * 3 + 2) * NP * 64 + e] = __builtin_bit_cast(v4u, tl);
+      }
+    }
+    // the other threads stage W_C, all of their loads issued first
+    constexpr int NCT = kFwdThreads - NTASK;
+    constexpr int NCI = (SH2 * 4 + NCT - 1) / NCT;
+    if (tid >= NTASK) {
+      v4f wv[NCI];
+#pragma unroll
+      for (int i = 0; i < NCI; ++i) {
+        const int f = min((tid - NTASK) + i * NCT, SH2 * 4 - 1);
+        wv[i] = ld4(WC + (size_t)(f >> 2) * D + sg * kGroup + 4 * (f & 3));
+      }
+#pragma unroll
+      for (int i = 0; i < NCI; ++i) {
+        const int f = min((tid - NTASK) + i * NCT, SH2 * 4 - 1);  // a clamped entry is written again
+        const int j = f >> 2, s4 = f & 3;
+        float* dst = reinterpret_cast<float*>(sWc);
+        const int jc = 2 * (j >> 5) + ((j & 7) >> 2);
+        const int jg = (j & 31) >> 3;
+        const int base = (jc * 64 + 16 * jg + 4 * s4) * 4 + (j & 3);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[base + 4 * q] = wv[i][q];
+      }
+    }
+  } else {
     constexpr int NW4 = SH2 * 4;  // float4s per matrix slab
     constexpr int NMAT = REPLAY ? 1 : 3;  // REPLAY: W_C only
     constexpr int M0 = 3 - NMAT;
@@ -310,10 +379,14 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     }
   }
   const T* hbase = H + (size_t)smp_a * K * SH2 + koff;
-  v4f hv[NKC];
-  // chunk kc (or pair kc/2) of history step t into hv
+  v4f hv[BFM ? 1 : NKC];
+  v4u hr[BFM ? NP : 1];  // BFM: raw bf16 pairs
+  // chunk kc (or pair kc/2) of history step t into hv (or hr)
   auto load_chunk = [&](int t, int kc) {
-    if constexpr (PAIR)
+    if constexpr (BFM)
+      hr[kc >> 1] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4u*>(hbase + (size_t)t * SH2 + (kc >> 1) * 32));
+    else if constexpr (PAIR)
       ld8_bf16(hbase + (size_t)t * SH2 + (kc >> 1) * 32, hv[kc], hv[kc + 1]);
     else
       hv[kc] = ld4_in(hbase + (size_t)t * SH2 + kc * 16);
@@ -369,6 +442,17 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) sC[half][wave][(4 * kg + r) * kGroup + m] = acc[r];
   }
+  if constexpr (BFM) {
+    // sum the readout now: the partials' memory is sXa's
+    __syncthreads();
+    if (scanner) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kFwdWaves; ++w) s += sC[half][w][smp * kGroup + m];
+      c = s;
+    }
+    __syncthreads();
+  }
 
   float G[kChunk];
   float Gr[kRegRounds];  // gate product of each round (rounds >= kRegRounds park theirs in saved)
@@ -395,6 +479,27 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
           pa = ld4(sv + (size_t)(2 * (t + kChunk)) * kPlane + toff);
           pb = ld4(sv + (size_t)(2 * (t + kChunk) + 1) * kPlane + toff);
         }
+      } else if constexpr (BFM) {
+#pragma unroll
+      for (int kc = 0; kc < NKC; kc += 2) {
+        const int pp = kc >> 1;
+        const v8bf h = __builtin_bit_cast(v8bf, hr[pp]);
+#pragma unroll
+        for (int tm = 0; tm < 3; ++tm) {
+          acca = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              h, __builtin_bit_cast(v8bf, sWab[(0 * 3 + tm) * NP * 64 + pp * 64 + lane]), acca, 0, 0, 0);
+          accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              h, __builtin_bit_cast(v8bf, sWab[(1 * 3 + tm) * NP * 64 + pp * 64 + lane]), accb, 0, 0, 0);
+        }
+        // keep PF chunks (PF/2 pairs) of this step in flight
+        if (kc + PF < NKC) load_chunk(t, kc + PF);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // next round's first loads go out before this round's exchange and scan
+      if (t + kChunk < t1) {
+#pragma unroll
+        for (int kc = 0; kc < PF; kc += 2) load_chunk(t + kChunk, kc);
+      }
       } else {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
@@ -444,7 +549,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 
     if (scanner) {
       const int idx = smp * kGroup + m;
-      if (ch == r0) {
+      if (!BFM && ch == r0) {
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kFwdWaves; ++w) s += sC[half][w][idx];

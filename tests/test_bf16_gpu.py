@@ -1,11 +1,12 @@
 """The bfloat16 trunk-input entry points (h_history, h_s2 as bf16) on an MI355X.
 
 The oracle runs on the same bf16-rounded values, so the tolerances are the
-fp32 path's.  Each bf16 value widens to fp32 exactly; the forward then sums
-the features in another order (a lane loads eight bf16 features at once), so
-against the fp32 entry points fed the widened values the results agree to
-fp32 rounding (checked at 1e-5), and the backward, whose order is the same,
-bit for bit.
+fp32 path's.  The forward multiplies the bf16 values with bf16 MFMAs against
+weights split exactly into three bf16 terms (every product exact, the sums
+in fp32, in another order than the fp32 path's), so against the fp32 entry
+points fed the widened values the results agree to fp32 rounding (checked at
+1e-5); the backward widens each bf16 value to fp32 exactly and sums in the
+same order, so it agrees bit for bit.
 """
 from __future__ import annotations
 
