@@ -177,7 +177,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     const T* __restrict__ H, const T* __restrict__ hs2,
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
     const float* __restrict__ stab, float* __restrict__ ctx, float* __restrict__ saved,
-    int L, int C, int mode) {
+    int L, int C, int mode, const float* __restrict__ tw, float* __restrict__ he) {
   constexpr int SH2 = NKC * 16;
   constexpr int kFwdBlocks = fwd_blocks(NKC);
   constexpr int kFwdThreads = fwd_threads(NKC);
@@ -620,6 +620,35 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       st4_nt(rs, off + kPlane * sizeof(float), mode == 1 ? sb : be);
     }
   } while (++ch < r1);
+
+  // The h_enriched blend (one state group: every state of these samples is
+  // here): he[b][j] = h_s2[b][j] + w_j * (sum_s context[b][s]) / D, by the
+  // work-group that writes context.  The h_s2 rows are read again here
+  // rather than kept in registers through the rounds.
+  if constexpr (!PAIR) {
+    if (he != nullptr && NG == 1 && cidx == C - 1) {  // uniform over the work-group
+      if (scanner) sC[half][0][smp * kGroup + m] = c * x;
+      __syncthreads();
+      float sum = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < kGroup; ++s2) sum += sC[half][0][m * kGroup + s2];  // states in order
+      const float scale = sum * (1.f / (float)kGroup);                         // exact: D = 16
+      const int b_row = blk * kBlock + m;
+#pragma unroll
+      for (int r = 0; r < NCR; ++r) {
+        const int kc = wave + kFwdWaves * r;
+        if (kc < NKC && b_row < B && blk_ok) {
+          const int f0 = kc * 16 + 4 * kg;
+          const v4f wv = tw != nullptr ? ld4(tw + f0) : v4f{1.f, 1.f, 1.f, 1.f};
+          const v4f hv2 = ld4_stream(hs2 + (size_t)b_row * SH2 + f0);
+          v4f o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = hv2[q] + wv[q] * scale;
+          __builtin_nontemporal_store(o, reinterpret_cast<v4f*>(he + (size_t)b_row * SH2 + f0));
+        }
+      }
+    }
+  }
 
   if (!scanner) return;
 
@@ -1430,7 +1459,8 @@ void fwd_chunks(const Plan& pl, int* L, int* C) {
 
 template <int NKC, class T>
 void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const float* WB,
-                const float* WC, const float* stab, float* ctx, float* saved, hipStream_t st) {
+                const float* WC, const float* stab, float* ctx, float* saved, hipStream_t st,
+                const float* tw, float* he) {
   int L, C;
   fwd_chunks(pl, &L, &C);
   constexpr int kFwdBlocks = fwd_blocks(NKC);
@@ -1439,14 +1469,14 @@ void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const
   const int grid = 8 * pl.NG * C * ((pairs + 7) / 8);
   if (C == 1) {
     hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
-                       H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 0);
+                       H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 0, tw, he);
     return;
   }
   hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
-                     hs2, WA, WB, WC, stab, ctx, saved, L, C, 1);
+                     hs2, WA, WB, WC, stab, ctx, saved, L, C, 1, nullptr, nullptr);
   hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG), dim3(kPlane), 0, st, pl.NB * pl.NG, pl.K, L, C, saved);
   hipLaunchKernelGGL((fwd_kernel<NKC, T, true>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
-                     H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 2);
+                     H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 2, tw, he);
 }
 
 int check_bwd_common(const Plan& pl, const void* H, const void* hs2, const void* saved, size_t saved_bytes,
@@ -1499,17 +1529,18 @@ int check_fwd(const Plan& pl, const void* H, const void* hs2, const float* WA, c
 
 template <class T>
 int run_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const float* WB, const float* WC,
-            const float* stab, float* ctx, void* saved, hipStream_t s) {
+            const float* stab, float* ctx, void* saved, hipStream_t s, const float* tw = nullptr,
+            float* he = nullptr) {
   float* sv = static_cast<float*>(saved);
   switch (pl.SH2 / 64) {
-    case 1: launch_fwd<4, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 2: launch_fwd<8, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 3: launch_fwd<12, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 4: launch_fwd<16, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 5: launch_fwd<20, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 6: launch_fwd<24, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 7: launch_fwd<28, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
-    case 8: launch_fwd<32, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s); break;
+    case 1: launch_fwd<4, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s, tw, he); break;
+    case 2: launch_fwd<8, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s, tw, he); break;
+    case 3: launch_fwd<12, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s, tw, he); break;
+    case 4: launch_fwd<16, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s, tw, he); break;
+    case 5: launch_fwd<20, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s, tw, he); break;
+    case 6: launch_fwd<24, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s, tw, he); break;
+    case 7: launch_fwd<28, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s, tw, he); break;
+    case 8: launch_fwd<32, T>(pl, H, hs2, WA, WB, WC, stab, ctx, sv, s, tw, he); break;
     default: return MAMBA2_SCAN_EUNSUPPORTED;
   }
   return launch_status();
@@ -1597,8 +1628,11 @@ int mamba2_scan_fwd_blend(int B, int K, int SH2, int STATE_D, const float* h_his
   if (st != MAMBA2_SCAN_OK) return st;
   if (!aligned4(stability) || !aligned16(temporal_weight) || !aligned16(h_enriched)) return MAMBA2_SCAN_EALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_fwd(pl, h_history, h_s2, W_A, W_B, W_C, stability, context, saved, s);
-  if (st != MAMBA2_SCAN_OK || h_enriched == nullptr) return st;
+  // one state group: the forward kernel writes h_enriched itself
+  const bool fused = pl.NG == 1 && h_enriched != nullptr;
+  st = run_fwd(pl, h_history, h_s2, W_A, W_B, W_C, stability, context, saved, s, fused ? temporal_weight : nullptr,
+               fused ? h_enriched : nullptr);
+  if (st != MAMBA2_SCAN_OK || h_enriched == nullptr || fused) return st;
   launch_blend_fwd(pl, context, h_s2, temporal_weight, h_enriched, s);
   return launch_status();
 }
