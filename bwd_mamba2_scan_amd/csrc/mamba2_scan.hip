@@ -779,12 +779,13 @@ struct BwdCtx {
 
 
 // Every unit issues the same loads, from addresses chosen by select: a step
-// unit reads alpha'_t, beta'_t, S_r and four H rows; the readout reads x_K
-// (three times) and four h_s2 rows.  With no memory operation under a branch
+// unit reads alpha'_t, beta'_t, S_r (ROUNDS: K spans several rounds) and
+// four H rows; the readout reads x_K (in each plane's place) and four h_s2
+// rows.  With no memory operation under a branch
 // the compiler's memory-counter waits stay exact, so the next unit's loads
 // (issued before this unit is consumed) stay in flight.  Rows of samples past
 // B (last block only) re-read a valid row; their d_context is masked to zero.
-template <class T>
+template <bool ROUNDS, class T>
 __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, int lane) {
   // unit u of the work-group's slice: block and step (t == K: the readout)
   const int ug = c.u0 + u;
@@ -796,10 +797,12 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, 
   const float* sv = c.saved + ((size_t)q.blk * c.NG + c.sg) * c.blk_stride;
   const int p0 = step ? 2 * q.t : 2 * c.K;
   const int p1 = step ? 2 * q.t + 1 : 2 * c.K;
-  const int ps = (c.rounds && step) ? 2 * c.K + 1 + q.t / kChunk : 2 * c.K;  // a valid plane either way
   U.al = ld4(sv + (size_t)p0 * kPlane + 4 * lane);
   U.be = ld4(sv + (size_t)p1 * kPlane + 4 * lane);
-  U.sr = ld4(sv + (size_t)ps * kPlane + 4 * lane);
+  if constexpr (ROUNDS) {
+    const int ps = step ? 2 * c.K + 1 + q.t / kChunk : 2 * c.K;  // a valid plane either way
+    U.sr = ld4(sv + (size_t)ps * kPlane + 4 * lane);
+  }
   const T* rows = step ? c.H + (size_t)q.t * c.SH2 : c.hs2;
   const size_t rstride = step ? (size_t)c.K * c.SH2 : (size_t)c.SH2;  // elements between samples
   const long long hk = step ? c.hk_step : c.hk_out;
@@ -814,7 +817,7 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, 
 
 // DBG: also store d_a, d_b, d_c (a separate instantiation, so the product
 // path carries no stores and no branches for them).
-template <bool DBG, class Ctx>
+template <bool DBG, bool ROUNDS, class Ctx>
 __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const Ctx& c, v4f (&acc)[4][3],
                                             float* __restrict__ d_a_out, float* __restrict__ d_b_out,
                                             float* __restrict__ d_c_out, bool write_dbg) {
@@ -824,7 +827,7 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = live && 4 * c.kg + i < q.nvalid;
-      const float dc = ok ? (c.rounds ? U.dc[i] * U.sr[i] : U.dc[i]) : 0.f;
+      const float dc = ok ? (ROUNDS ? U.dc[i] * U.sr[i] : U.dc[i]) : 0.f;
       const float da = dc * U.al[i];
       const float db = dc * U.be[i];
       if (DBG && write_dbg && ok) {
@@ -850,7 +853,7 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
   }
 }
 
-template <class T, bool DBG>
+template <class T, bool DBG, bool ROUNDS>
 __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
     int B, int K, int SH2, int NG, int NB, int P, int UPW,
     const T* __restrict__ H, const T* __restrict__ hs2,
@@ -912,14 +915,14 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   // each unit's registers keep one role.
   BwdUnit R0, R1;
   int u = wave;
-  bwd_load(R0, min(u, n - 1), c, lane);
+  bwd_load<ROUNDS>(R0, min(u, n - 1), c, lane);
   for (; u < n; u += 2 * S) {
-    bwd_load(R1, min(u + S, n - 1), c, lane);
+    bwd_load<ROUNDS>(R1, min(u + S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
-    bwd_compute<DBG>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
-    bwd_load(R0, min(u + 2 * S, n - 1), c, lane);
+    bwd_compute<DBG, ROUNDS>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    bwd_load<ROUNDS>(R0, min(u + 2 * S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
-    bwd_compute<DBG>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    bwd_compute<DBG, ROUNDS>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
   }
 
   // Result lane (g = kg, n = m), element r of tile q: feature row
@@ -1502,7 +1505,9 @@ template <class T>
 void launch_partials(const Plan& pl, const T* H, const T* hs2, const void* saved, const float* dctx,
                      float* da, float* db, float* dc, void* ws, hipStream_t st) {
   const int grid = 8 * pl.V * ((pl.P + 7) / 8);
-  auto kern = (da || db || dc) ? bwd_partials_kernel<T, true> : bwd_partials_kernel<T, false>;
+  const bool dbg = da || db || dc, rounds = pl.K > kChunk;
+  auto kern = dbg ? (rounds ? bwd_partials_kernel<T, true, true> : bwd_partials_kernel<T, true, false>)
+                  : (rounds ? bwd_partials_kernel<T, false, true> : bwd_partials_kernel<T, false, false>);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
                      pl.NB, pl.P, pl.UPW, H, hs2, static_cast<const float*>(saved), dctx, da, db, dc,
                      static_cast<float*>(ws));
