@@ -102,6 +102,7 @@ __device__ __forceinline__ v4f ld4_in<float>(const float* p) {
 // two groups of four.
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void ld8_bf16(const bf16_t* p, v4f& lo, v4f& hi) {
   const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
   lo[0] = __uint_as_float(w[0] << 16);
@@ -753,6 +754,7 @@ __global__ __launch_bounds__(256) void fwd_carry_kernel(int NBG, int K, int L, i
 // only.
 struct BwdUnit {
   v4f h[4];   // A operands: 4 rows (samples 4kg+i) x 4 features
+  v2u hr[4];  // bf16 inputs: the same, as loaded (four bf16 per row)
   v4f al;     // alpha'_t (step unit) or x_K (readout unit), samples 4kg..4kg+3
   v4f be;     // beta'_t (step unit)
   v4f sr;     // S_r of the step's round (1 when K fits one round)
@@ -810,19 +812,95 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, 
   for (int i = 0; i < 4; ++i) {
     const int s0 = min(q.blk * kBlock + i, c.B - 1);  // row i of the block (scalar)
     const bool ok = 4 * c.kg + i < q.nvalid;
-    U.h[i] = ld4_in(rows + (size_t)s0 * rstride + (ok ? hk : 0) + c.col);
+    const T* hp = rows + (size_t)s0 * rstride + (ok ? hk : 0) + c.col;
+    if constexpr (sizeof(T) == 2)
+      U.hr[i] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(hp));
+    else
+      U.h[i] = ld4_in(hp);
     U.dc[i] = c.dctx[(size_t)s0 * c.D + (ok ? 4 * c.kg * c.D : 0) + c.state];
   }
 }
 
 // DBG: also store d_a, d_b, d_c (a separate instantiation, so the product
 // path carries no stores and no branches for them).
-template <bool DBG, bool ROUNDS, class Ctx>
+// bf16 history: one v_mfma_f32_16x16x16_bf16 per tile and term covers all
+// 16 samples of the unit.  Its A operand (feature 4m+q, samples 4kg..4kg+3)
+// is gathered from the four rows this lane loaded; its B operand is d split
+// exactly into three bf16 terms, so every product is exact and only the
+// fp32 accumulation rounds.
+__device__ __forceinline__ void bf16_split3(const float (&d)[4], v4bf (&t)[3]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 hi = (__bf16)d[i];
+    const float r1 = d[i] - (float)hi;
+    const __bf16 mi = (__bf16)r1;
+    t[0][i] = hi;
+    t[1][i] = mi;
+    t[2][i] = (__bf16)(r1 - (float)mi);
+  }
+}
+__device__ __forceinline__ void bf16_tiles(const BwdUnit& U, v4bf (&a)[4]) {
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int w = qq >> 1, sh = (qq & 1) * 16;
+    v2u p;
+    p[0] = ((U.hr[0][w] >> sh) & 0xffffu) | (((U.hr[1][w] >> sh) & 0xffffu) << 16);
+    p[1] = ((U.hr[2][w] >> sh) & 0xffffu) | (((U.hr[3][w] >> sh) & 0xffffu) << 16);
+    a[qq] = __builtin_bit_cast(v4bf, p);
+  }
+}
+
+template <bool DBG, bool ROUNDS, bool BF, class Ctx>
 __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const Ctx& c, v4f (&acc)[4][3],
                                             float* __restrict__ d_a_out, float* __restrict__ d_b_out,
                                             float* __restrict__ d_c_out, bool write_dbg) {
   const BwdUnit& q = U;
   const int sbase = q.blk * kBlock + 4 * c.kg;
+  if constexpr (BF) {
+    v4bf a[4];
+    bf16_tiles(U, a);
+    if (q.t < c.K) {
+      float da[4], db[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = live && 4 * c.kg + i < q.nvalid;
+        const float dc = ok ? (ROUNDS ? U.dc[i] * U.sr[i] : U.dc[i]) : 0.f;
+        da[i] = dc * U.al[i];
+        db[i] = dc * U.be[i];
+        if (DBG && write_dbg && ok) {
+          const int s = sbase + i;
+          if (d_a_out) d_a_out[((size_t)s * c.K + q.t) * c.D + c.state] = da[i];
+          if (d_b_out) d_b_out[((size_t)s * c.K + q.t) * c.D + c.state] = db[i];
+        }
+      }
+      v4bf ta[3], tb[3];
+      bf16_split3(da, ta);
+      bf16_split3(db, tb);
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          acc[qq][0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[qq], ta[tm], acc[qq][0], 0, 0, 0);
+          acc[qq][1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[qq], tb[tm], acc[qq][1], 0, 0, 0);
+        }
+    } else {
+      float dd[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = live && 4 * c.kg + i < q.nvalid;
+        dd[i] = (ok ? U.dc[i] : 0.f) * U.al[i];
+        if (DBG && write_dbg && ok && d_c_out) d_c_out[(size_t)(sbase + i) * c.D + c.state] = dd[i];
+      }
+      v4bf td[3];
+      bf16_split3(dd, td);
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          acc[qq][2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[qq], td[tm], acc[qq][2], 0, 0, 0);
+    }
+    return;
+  }
   if (q.t < c.K) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -919,10 +997,10 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   for (; u < n; u += 2 * S) {
     bwd_load<ROUNDS>(R1, min(u + S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
-    bwd_compute<DBG, ROUNDS>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
     bwd_load<ROUNDS>(R0, min(u + 2 * S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
-    bwd_compute<DBG, ROUNDS>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
   }
 
   // Result lane (g = kg, n = m), element r of tile q: feature row

@@ -1,12 +1,12 @@
 """The bfloat16 trunk-input entry points (h_history, h_s2 as bf16) on an MI355X.
 
 The oracle runs on the same bf16-rounded values, so the tolerances are the
-fp32 path's.  The forward multiplies the bf16 values with bf16 MFMAs against
-weights split exactly into three bf16 terms (every product exact, the sums
-in fp32, in another order than the fp32 path's), so against the fp32 entry
-points fed the widened values the results agree to fp32 rounding (checked at
-1e-5); the backward widens each bf16 value to fp32 exactly and sums in the
-same order, so it agrees bit for bit.
+fp32 path's.  Both passes multiply the bf16 values with bf16 MFMAs against
+the other operand split exactly into three bf16 terms (the weights in the
+forward, d_a/d_b/d_c in the backward): every product is exact and the sums
+run in fp32, in another order than the fp32 path's, so against the fp32
+entry points fed the widened values the results agree to fp32 rounding
+(checked at 1e-5).
 """
 from __future__ import annotations
 
@@ -60,12 +60,13 @@ def check(inputs, debug=True):
     assert_elementwise(ctx.cpu().numpy(), ctx32.cpu().numpy().astype(np.float64), "context vs fp32 path", tol=1e-5)
     for name in ("dW_A", "dW_B", "dW_C"):
         assert_l1(g[name].cpu().numpy(), g32[name].cpu().numpy().astype(np.float64), name + " vs fp32 path", tol=1e-5)
-    # the backward alone, on one forward's saved terms: the same bits
+    # the backward alone, on one forward's saved terms: fp32 rounding apart
     g16b = m2.bwd(t16["h_history"], t16["h_s2"], saved32, t16["d_context"])
     g32b = m2.bwd(t32["h_history"], t32["h_s2"], saved32, t32["d_context"])
     torch.cuda.synchronize()
     for name in ("dW_A", "dW_B", "dW_C"):
-        assert torch.equal(g16b[name], g32b[name]), name
+        assert_l1(g16b[name].cpu().numpy(), g32b[name].cpu().numpy().astype(np.float64), name + " (bwd alone)",
+                  tol=1e-5)
 
 
 @pytest.mark.parametrize("B,K,SH2,D", EDGE_SHAPES, ids=lambda v: str(v))
