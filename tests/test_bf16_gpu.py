@@ -84,6 +84,13 @@ def test_bf16_large(name):
     check(workload_inputs(name), debug=False)
 
 
+@pytest.mark.parametrize("B,K,SH2,D", [(64, 1024, 256, 16), (3, 300, 64, 64), (17, 160, 192, 16)],
+                         ids=lambda v: str(v))
+def test_bf16_chunked_history(B, K, SH2, D):
+    """Few samples, long histories: the chunked forward (summary, carry, replay) with bf16 inputs."""
+    check(make_inputs(B, K, SH2, D, seed=B + K + 5, gate_bias=2.0), debug=(K <= 300))
+
+
 def test_bf16_split_phase_matches():
     inputs = make_inputs(300, 9, 192, 32, seed=77)
     t16, _, _ = split(inputs)
