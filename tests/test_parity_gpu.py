@@ -215,16 +215,20 @@ def test_workloads_table_matches_pages_shape():
     assert (w.B, w.K, w.SH2, w.D) == (8192, 8, 256, 16)
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("B,K,SH2,D,bf16", [(300, 8, 256, 32, False), (17, 160, 192, 16, False),
+                                             (300, 8, 256, 16, True), (17, 160, 192, 16, True)],
+                         ids=lambda v: str(v))
+def test_graph_replays_match_eager(B, K, SH2, D, bf16):
     """fwd + bwd captured in a HIP graph and replayed several times, with eager
     work and synchronisation between replays, give the eager bits every time
-    (the library enqueues no memset and allocates nothing, so it is capturable)."""
-    inp = make_inputs(300, 8, 256, 32, seed=21)
+    (the library enqueues no memset and allocates nothing, so it is capturable).
+    The second shape takes the chunked forward (summary, carry, replay)."""
+    inp = make_inputs(B, K, SH2, D, seed=21, gate_bias=2.0 if K > 8 else 0.0)
     t = _to_dev(inp)
-    B, K, SH2 = inp["h_history"].shape
-    D = inp["W_A"].shape[1]
+    if bf16:
+        for k in ("h_history", "h_s2"):
+            t[k] = t[k].to(torch.bfloat16)
     dev = t["h_history"].device
-    eager = run_gpu(t)
 
     ctx = torch.empty((B, D), device=dev)
     saved = m2.alloc_saved(B, K, SH2, D, dev)
@@ -235,13 +239,16 @@ def test_graph_replays_match_eager():
         m2.fwd(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], context=ctx, saved=saved)
         m2.bwd(t["h_history"], t["h_s2"], saved, t["d_context"], workspace=ws, out=out)
     torch.cuda.synchronize()
+    eager = {"context": ctx.cpu().numpy().copy()}
+    eager.update({k: v.cpu().numpy().copy() for k, v in out.items()})
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         m2.fwd(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"], context=ctx, saved=saved)
         m2.bwd(t["h_history"], t["h_s2"], saved, t["d_context"], workspace=ws, out=out)
     for rep in range(4):
-        # scribble over the outputs eagerly, then replay
+        # scribble over the outputs and the saved terms eagerly, then replay
         ctx.fill_(float("nan"))
+        saved.fill_(float("nan"))
         for v in out.values():
             v.fill_(float("nan"))
         torch.cuda.synchronize()
