@@ -206,9 +206,12 @@ int mamba2_scan_bwd_blend(int B, int K, int SH2, int STATE_D,
 /*
  * Reduced-precision trunk inputs: h_history and h_s2 hold bfloat16 values
  * (their 16-bit patterns, the top half of the fp32 with the same value),
- * halving the bytes of the dominant reads.  Every other argument, the
- * arithmetic (fp32, widening each input exactly) and the results are as for
- * the fp32 entry point of the same name: mamba2_scan_fwd,
+ * halving the bytes of the dominant reads.  The bf16 values meet bf16
+ * matrix instructions whose other operand (the weights in the forward,
+ * d_a/d_b/d_c in the backward) is split exactly into three bf16 terms, so
+ * every product is exact in fp32 and every sum accumulates in fp32: results
+ * agree with the fp32 entry point of the same name, fed the same values,
+ * to fp32 rounding.  Every other argument is as for mamba2_scan_fwd,
  * mamba2_scan_bwd_partials and mamba2_scan_bwd.  The same `saved`,
  * workspace and second phase (mamba2_scan_bwd_reduce) serve both.
  * h_history and h_s2 must be 16-byte aligned.
