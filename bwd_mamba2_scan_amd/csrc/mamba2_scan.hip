@@ -707,25 +707,59 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 // S plane of its first round) to the state it starts from,
 //   x_start(0) = 0,  x_start(c+1) = G_c x_start(c) + X_c,
 // (second S plane) and the product of every later chunk's gates (first).
+// The summaries are read a batch of chunks at a time, every load of a batch
+// in flight together (the recurrence itself is a few FMAs per chunk); with
+// at most one batch of chunks, the suffix products reuse the gates in
+// registers.
+constexpr int kCarryBatch = 64;
+
 __global__ __launch_bounds__(256) void fwd_carry_kernel(int NBG, int K, int L, int C, float* __restrict__ saved) {
   const int bg = blockIdx.x;  // (block, state group)
   if (bg >= NBG) return;
   const int e = threadIdx.x;  // entry of the 16 x 16 plane
   float* sv = saved + (size_t)bg * saved_planes(K) * kPlane + e;
+  const int rpc = L / kChunk;  // rounds per chunk
+  auto gate = [&](int cc) { return sv + (size_t)(2 * K + 1 + cc * rpc) * kPlane; };
+  auto state = [&](int cc) { return sv + (size_t)(2 * K + 2 + cc * rpc) * kPlane; };
+  float G[kCarryBatch];
   float x = 0.f;
-  for (int cc = 0; cc < C; ++cc) {
-    float* p1 = sv + (size_t)(2 * K + 2 + cc * L / kChunk) * kPlane;
-    const float Gc = sv[(size_t)(2 * K + 1 + cc * L / kChunk) * kPlane];
-    const float Xc = *p1;
-    *p1 = x;
-    x = Gc * x + Xc;
+  for (int c0 = 0; c0 < C; c0 += kCarryBatch) {
+    float X[kCarryBatch];
+#pragma unroll
+    for (int i = 0; i < kCarryBatch; ++i) {  // clamped: every load unconditional
+      const int cc = min(c0 + i, C - 1);
+      G[i] = *gate(cc);
+      X[i] = *state(cc);
+    }
+#pragma unroll
+    for (int i = 0; i < kCarryBatch; ++i) {
+      if (c0 + i < C) {
+        *state(c0 + i) = x;
+        x = G[i] * x + X[i];
+      }
+    }
   }
   float S = 1.f;
-  for (int cc = C - 1; cc >= 0; --cc) {
-    float* p0 = sv + (size_t)(2 * K + 1 + cc * L / kChunk) * kPlane;
-    const float Gc = *p0;
-    *p0 = S;
-    S *= Gc;
+  if (C <= kCarryBatch) {
+#pragma unroll
+    for (int i = kCarryBatch - 1; i >= 0; --i) {
+      if (i < C) {
+        *gate(i) = S;
+        S *= G[i];
+      }
+    }
+    return;
+  }
+  for (int c1 = C; c1 > 0; c1 -= kCarryBatch) {
+#pragma unroll
+    for (int i = 0; i < kCarryBatch; ++i) G[i] = *gate(max(c1 - 1 - i, 0));
+#pragma unroll
+    for (int i = 0; i < kCarryBatch; ++i) {
+      if (c1 - 1 - i >= 0) {
+        *gate(c1 - 1 - i) = S;
+        S *= G[i];
+      }
+    }
   }
 }
 
