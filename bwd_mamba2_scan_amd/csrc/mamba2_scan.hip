@@ -193,17 +193,26 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 #endif
   constexpr int PFP = PAIR ? (FWD_PAIR_PF < NKC / 2 ? FWD_PAIR_PF : NKC / 2) : 0;  // pairs in flight
   constexpr int PF = PAIR ? 2 * PFP : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC);   // chunks in flight
+  static_assert(PAIR || PF % 2 == 0, "fp32 loads go in pairs");
   // bf16 trunk inputs feed bf16 MFMAs directly: each weight is split
   // exactly into three bf16 terms (hi + mid + lo == W for every fp32 W above
   // ~1e-33), so every product is exact and only the fp32 accumulation
   // rounds, as with fp32 MFMAs.  The readout keeps fp32 MFMAs on widened
   // h_s2.
   constexpr bool BFM = PAIR && !REPLAY;
+  // fp32 history (CT): each load instruction covers 8 rows x 128 contiguous
+  // bytes (lane (r8, p8): row r8 of one half of the block, features 4*p8 ..
+  // +3 of a 32-feature pair of chunks), which streams ~10 % faster than the
+  // MFMA operand order (16 rows x 64 B); the two loads of a pair go through
+  // a per-wave LDS tile into the operand order.  W_C then comes straight
+  // from memory for the readout (its slab's LDS holds the tiles).
+  constexpr bool CT = !PAIR && !REPLAY;
   constexpr int NP = NKC / 2;  // 32-feature pairs of chunks
   __shared__ v4f sWa[BFM ? 1 : NKC * 64];
   __shared__ v4f sWb[BFM ? 1 : NKC * 64];
   __shared__ v4u sWab[BFM ? 6 * NP * 64 : 1];  // [mat A|B][term hi|mid|lo][pair][lane]: 8 bf16
-  __shared__ v4f sWc[NKC * 64];
+  __shared__ v4f sWc[CT ? 1 : NKC * 64];
+  __shared__ v4f sT[CT ? kFwdBlocks * kFwdWaves * 128 : 1];  // CT: [wave][half j][64 slots]
   __shared__ float sXa[kFwdBlocks][kChunk][kPlane];
   __shared__ float sXb[kFwdBlocks][kChunk][kPlane];
   // readout partials; with BFM they share sXa's memory (summed into c
@@ -327,8 +336,8 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     }
   } else {
     constexpr int NW4 = SH2 * 4;  // float4s per matrix slab
-    constexpr int NMAT = REPLAY ? 1 : 3;  // REPLAY: W_C only
-    constexpr int M0 = 3 - NMAT;
+    constexpr int NMAT = REPLAY ? 1 : (CT ? 2 : 3);  // REPLAY: W_C only; CT: W_A, W_B
+    constexpr int M0 = REPLAY ? 2 : 0;
     constexpr int NWT = (NMAT * NW4 + kFwdThreads - 1) / kFwdThreads;
     v4f wr[NWT];
 #pragma unroll
@@ -379,7 +388,21 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       hc[r] = ld4_in(crow + kc * 16);
     }
   }
+  // CT: the readout's W_C operand, W_C[kc*16 + 4kg + i][sg*16 + m]
+  v4f wcv[CT ? NCR : 1];
+  if constexpr (CT) {
+#pragma unroll
+    for (int r = 0; r < NCR; ++r) {
+      const int kc = min(wave + kFwdWaves * r, NKC - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wcv[r][i] = WC[(size_t)(kc * 16 + 4 * kg + i) * D + sg * kGroup + m];
+    }
+  }
   const T* hbase = H + (size_t)smp_a * K * SH2 + koff;
+  // CT: lane (r8, p8) loads rows r8 and 8 + r8 of the block
+  const int r8 = lane >> 3, p8 = lane & 7;
+  const T* hb0 = H + (size_t)min(blk * kBlock + r8, B - 1) * K * SH2 + 4 * p8;
+  const T* hb1 = H + (size_t)min(blk * kBlock + 8 + r8, B - 1) * K * SH2 + 4 * p8;
   v4f hv[BFM ? 1 : NKC];
   v4u hr[BFM ? NP : 1];  // BFM: raw bf16 pairs
   // chunk kc (or pair kc/2) of history step t into hv (or hr)
@@ -389,9 +412,20 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
           reinterpret_cast<const v4u*>(hbase + (size_t)t * SH2 + (kc >> 1) * 32));
     else if constexpr (PAIR)
       ld8_bf16(hbase + (size_t)t * SH2 + (kc >> 1) * 32, hv[kc], hv[kc + 1]);
+    else if constexpr (CT)  // load kc: half kc & 1 of pair kc >> 1
+      hv[kc] = ld4_in(((kc & 1) ? hb1 : hb0) + (size_t)t * SH2 + (kc >> 1) * 32);
     else
       hv[kc] = ld4_in(hbase + (size_t)t * SH2 + kc * 16);
   };
+  // CT tile slots, XOR-swizzled so that the 16-byte writes of 8 lanes and the
+  // operand reads of 16 lanes each touch distinct banks: lane (r8, p8) of
+  // half j writes slot 64j + 8r8 + (p8 ^ r8 ^ j); operand lane (kg, m) of
+  // chunk h reads row m's features 16h + 4kg .. +3 of the pair.
+  v4f* tile = sT + (CT ? wg_wave * 128 : 0);
+  const int wslot0 = 8 * r8 + (p8 ^ r8);
+  const int wslot1 = 64 + 8 * r8 + (p8 ^ r8 ^ 1);
+  const int rslot0 = 64 * (m >> 3) + 8 * (m & 7) + ((0 + kg) ^ (m & 7) ^ (m >> 3));
+  const int rslot1 = 64 * (m >> 3) + 8 * (m & 7) + ((4 + kg) ^ (m & 7) ^ (m >> 3));
   // REPLAY: this wave's step projections, as float4s of the alpha'/beta'
   // slots (its four samples 4kg+r at state m are entries kg*64 + 4m + r,
   // the MFMA result layout)
@@ -435,7 +469,11 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       for (int r = 0; r < NCR; ++r) {
         const int kc = wave + kFwdWaves * r;
         const bool ok = kc < NKC;
-        const v4f bv = sWc[min(kc, NKC - 1) * 64 + lane];
+        v4f bv;
+        if constexpr (CT)
+          bv = wcv[r];
+        else
+          bv = sWc[min(kc, NKC - 1) * 64 + lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc = mfma16x16x4(ok ? hc[r][i] : 0.f, bv[i], acc);
       }
@@ -500,6 +538,38 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       if (t + kChunk < t1) {
 #pragma unroll
         for (int kc = 0; kc < PF; kc += 2) load_chunk(t + kChunk, kc);
+      }
+      } else if constexpr (CT) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        // the pair's two loads into this wave's tile, then back in operand order
+        tile[wslot0] = hv[2 * pp];
+        tile[wslot1] = hv[2 * pp + 1];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const v4f a0 = tile[rslot0];
+        const v4f a1 = tile[rslot1];
+        // keep PF loads of this step in flight
+        if (2 * pp + PF < NKC) load_chunk(t, 2 * pp + PF);
+        if (2 * pp + 1 + PF < NKC) load_chunk(t, 2 * pp + 1 + PF);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const v4f av = h ? a1 : a0;
+          const v4f wa = sWa[(2 * pp + h) * 64 + lane];
+          const v4f wb = sWb[(2 * pp + h) * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acca = mfma16x16x4(av[i], wa[i], acca);
+            accb = mfma16x16x4(av[i], wb[i], accb);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // next round's first loads go out before this round's exchange and scan
+      if (t + kChunk < t1) {
+#pragma unroll
+        for (int kc = 0; kc < PF; ++kc) load_chunk(t + kChunk, kc);
       }
       } else {
 #pragma unroll
