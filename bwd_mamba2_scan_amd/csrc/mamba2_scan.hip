@@ -184,14 +184,15 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   constexpr int kFwdThreads = fwd_threads(NKC);
   constexpr int NCR = (NKC + kFwdWaves - 1) / kFwdWaves;                   // readout chunks per wave
   constexpr int NCRP = (NKC / 2 + kFwdWaves - 1) / kFwdWaves;              // readout pairs per wave (bf16)
-  // bf16 inputs load in pairs of chunks: lane (kg, m) takes features
+  // bf16 inputs come in pairs of chunks: lane (kg, m) holds features
   // 32p + 8kg .. +7 of pair p, the first four for chunk 2p, the rest for
   // chunk 2p+1 (the weight slab is staged in the same order).
   constexpr bool PAIR = sizeof(T) == 2;
 #ifndef FWD_PAIR_PF
-#define FWD_PAIR_PF 3
+#define FWD_PAIR_PF 4
 #endif
   constexpr int PFP = PAIR ? (FWD_PAIR_PF < NKC / 2 ? FWD_PAIR_PF : NKC / 2) : 0;  // pairs in flight
+  static_assert(!PAIR || PFP % 2 == 0, "bf16 loads go in spans of two pairs");
   constexpr int PF = PAIR ? 2 * PFP : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC);   // chunks in flight
   static_assert(PAIR || PF % 2 == 0, "fp32 loads go in pairs");
   // bf16 trunk inputs feed bf16 MFMAs directly: each weight is split
@@ -200,13 +201,14 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // rounds, as with fp32 MFMAs.  The readout keeps fp32 MFMAs on widened
   // h_s2.
   constexpr bool BFM = PAIR && !REPLAY;
-  // fp32 history (CT): each load instruction covers 8 rows x 128 contiguous
-  // bytes (lane (r8, p8): row r8 of one half of the block, features 4*p8 ..
-  // +3 of a 32-feature pair of chunks), which streams ~10 % faster than the
-  // MFMA operand order (16 rows x 64 B); the two loads of a pair go through
-  // a per-wave LDS tile into the operand order.  W_C then comes straight
-  // from memory for the readout (its slab's LDS holds the tiles).
-  constexpr bool CT = !PAIR && !REPLAY;
+  // History loads (CT): each load instruction covers 8 rows x 128 contiguous
+  // bytes (lane (r8, p8): row r8 of one half of the block, 16 bytes at 16*p8
+  // of a 128-byte span: 32 fp32 or 64 bf16 features), which streams ~10 %
+  // faster than the MFMA operand order (16 rows x 64 B); the two halves of
+  // a span go through a per-wave LDS tile into the operand order.  W_C then
+  // comes straight from memory for the readout (its slab's LDS holds the
+  // tiles).
+  constexpr bool CT = !REPLAY;
   constexpr int NP = NKC / 2;  // 32-feature pairs of chunks
   __shared__ v4f sWa[BFM ? 1 : NKC * 64];
   __shared__ v4f sWb[BFM ? 1 : NKC * 64];
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   if constexpr (BFM) {
     // W_A, W_B: a task is (matrix, octet o of rows 8o..8o+7, states
     // 4*s4..4*s4+3); per state n it writes the eight rows' three terms as
-    // three 16-byte entries (pair o/4, lane (o%4, n)).  W_C as for fp32.
+    // three 16-byte entries (pair o/4, lane (o%4, n)).
     constexpr int NTASK = 2 * (SH2 / 8) * 4;  // = SH2 <= half the threads
     static_assert(2 * NTASK <= kFwdThreads, "one task per thread");
     if (tid < NTASK) {
@@ -310,28 +312,6 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
         sWab[(mat * 3 + 0) * NP * 64 + e] = __builtin_bit_cast(v4u, th);
         sWab[(mat * 3 + 1) * NP * 64 + e] = __builtin_bit_cast(v4u, tm);
         sWab[(mat * 3 + 2) * NP * 64 + e] = __builtin_bit_cast(v4u, tl);
-      }
-    }
-    // the other threads stage W_C, all of their loads issued first
-    constexpr int NCT = kFwdThreads - NTASK;
-    constexpr int NCI = (SH2 * 4 + NCT - 1) / NCT;
-    if (tid >= NTASK) {
-      v4f wv[NCI];
-#pragma unroll
-      for (int i = 0; i < NCI; ++i) {
-        const int f = min((tid - NTASK) + i * NCT, SH2 * 4 - 1);
-        wv[i] = ld4(WC + (size_t)(f >> 2) * D + sg * kGroup + 4 * (f & 3));
-      }
-#pragma unroll
-      for (int i = 0; i < NCI; ++i) {
-        const int f = min((tid - NTASK) + i * NCT, SH2 * 4 - 1);  // a clamped entry is written again
-        const int j = f >> 2, s4 = f & 3;
-        float* dst = reinterpret_cast<float*>(sWc);
-        const int jc = 2 * (j >> 5) + ((j & 7) >> 2);
-        const int jg = (j & 31) >> 3;
-        const int base = (jc * 64 + 16 * jg + 4 * s4) * 4 + (j & 3);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[base + 4 * q] = wv[i][q];
       }
     }
   } else {
@@ -388,9 +368,20 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       hc[r] = ld4_in(crow + kc * 16);
     }
   }
-  // CT: the readout's W_C operand, W_C[kc*16 + 4kg + i][sg*16 + m]
-  v4f wcv[CT ? NCR : 1];
-  if constexpr (CT) {
+  // CT: the readout's W_C operand, W_C[f + i][sg*16 + m] for the features
+  // f + i (i = 0..3) that this lane's h_s2 values carry
+  v4f wcv[CT ? (PAIR ? 2 * NCRP : NCR) : 1];
+  if constexpr (CT && PAIR) {
+#pragma unroll
+    for (int r = 0; r < NCRP; ++r) {
+      const int pc = min(wave + kFwdWaves * r, NKC / 2 - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          wcv[2 * r + h][i] = WC[(size_t)(pc * 32 + 8 * kg + 4 * h + i) * D + sg * kGroup + m];
+    }
+  } else if constexpr (CT) {
 #pragma unroll
     for (int r = 0; r < NCR; ++r) {
       const int kc = min(wave + kFwdWaves * r, NKC - 1);
@@ -401,15 +392,15 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   const T* hbase = H + (size_t)smp_a * K * SH2 + koff;
   // CT: lane (r8, p8) loads rows r8 and 8 + r8 of the block
   const int r8 = lane >> 3, p8 = lane & 7;
-  const T* hb0 = H + (size_t)min(blk * kBlock + r8, B - 1) * K * SH2 + 4 * p8;
-  const T* hb1 = H + (size_t)min(blk * kBlock + 8 + r8, B - 1) * K * SH2 + 4 * p8;
+  const T* hb0 = H + (size_t)min(blk * kBlock + r8, B - 1) * K * SH2 + (16 / sizeof(T)) * p8;
+  const T* hb1 = H + (size_t)min(blk * kBlock + 8 + r8, B - 1) * K * SH2 + (16 / sizeof(T)) * p8;
   v4f hv[BFM ? 1 : NKC];
   v4u hr[BFM ? NP : 1];  // BFM: raw bf16 pairs
   // chunk kc (or pair kc/2) of history step t into hv (or hr)
   auto load_chunk = [&](int t, int kc) {
-    if constexpr (BFM)
+    if constexpr (BFM)  // load kc/2: half (kc/2) & 1 of the 64-feature span kc/4
       hr[kc >> 1] = __builtin_nontemporal_load(
-          reinterpret_cast<const v4u*>(hbase + (size_t)t * SH2 + (kc >> 1) * 32));
+          reinterpret_cast<const v4u*>((((kc >> 1) & 1) ? hb1 : hb0) + (size_t)t * SH2 + (kc >> 2) * 64));
     else if constexpr (PAIR)
       ld8_bf16(hbase + (size_t)t * SH2 + (kc >> 1) * 32, hv[kc], hv[kc + 1]);
     else if constexpr (CT)  // load kc: half kc & 1 of pair kc >> 1
@@ -417,10 +408,11 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     else
       hv[kc] = ld4_in(hbase + (size_t)t * SH2 + kc * 16);
   };
-  // CT tile slots, XOR-swizzled so that the 16-byte writes of 8 lanes and the
-  // operand reads of 16 lanes each touch distinct banks: lane (r8, p8) of
-  // half j writes slot 64j + 8r8 + (p8 ^ r8 ^ j); operand lane (kg, m) of
-  // chunk h reads row m's features 16h + 4kg .. +3 of the pair.
+  // CT tile slots (16 bytes each), XOR-swizzled so that the writes of 8
+  // lanes and the operand reads of 16 lanes each touch distinct banks: lane
+  // (r8, p8) of half j writes slot 64j + 8r8 + (p8 ^ r8 ^ j); operand lane
+  // (kg, m) of half-span h (fp32: chunk h of the pair; bf16: pair h of the
+  // span) reads row m's 16 bytes at 16*(4h + kg).
   v4f* tile = sT + (CT ? wg_wave * 128 : 0);
   const int wslot0 = 8 * r8 + (p8 ^ r8);
   const int wslot1 = 64 + 8 * r8 + (p8 ^ r8 ^ 1);
@@ -459,7 +451,11 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
         const int pcc = min(pc, NKC / 2 - 1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const v4f bv = sWc[(2 * pcc + h) * 64 + lane];
+          v4f bv;
+          if constexpr (CT)
+            bv = wcv[2 * r + h];
+          else
+            bv = sWc[(2 * pcc + h) * 64 + lane];
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc = mfma16x16x4(ok ? hc[2 * r + h][i] : 0.f, bv[i], acc);
         }
@@ -520,18 +516,31 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
         }
       } else if constexpr (BFM) {
 #pragma unroll
-      for (int kc = 0; kc < NKC; kc += 2) {
-        const int pp = kc >> 1;
-        const v8bf h = __builtin_bit_cast(v8bf, hr[pp]);
+      for (int q4 = 0; q4 < NP / 2; ++q4) {
+        // the span's two loads into this wave's tile, then back as the
+        // operands of pairs 2*q4 and 2*q4 + 1
+        tile[wslot0] = __builtin_bit_cast(v4f, hr[2 * q4]);
+        tile[wslot1] = __builtin_bit_cast(v4f, hr[2 * q4 + 1]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const v4f h0 = tile[rslot0];
+        const v4f h1 = tile[rslot1];
+        // keep PFP loads of this step in flight
+        if (2 * q4 + PFP < NP) load_chunk(t, 2 * (2 * q4 + PFP));
+        if (2 * q4 + 1 + PFP < NP) load_chunk(t, 2 * (2 * q4 + 1 + PFP));
 #pragma unroll
-        for (int tm = 0; tm < 3; ++tm) {
-          acca = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              h, __builtin_bit_cast(v8bf, sWab[(0 * 3 + tm) * NP * 64 + pp * 64 + lane]), acca, 0, 0, 0);
-          accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              h, __builtin_bit_cast(v8bf, sWab[(1 * 3 + tm) * NP * 64 + pp * 64 + lane]), accb, 0, 0, 0);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int pp = 2 * q4 + hh;
+          const v8bf h = __builtin_bit_cast(v8bf, hh ? h1 : h0);
+#pragma unroll
+          for (int tm = 0; tm < 3; ++tm) {
+            acca = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                h, __builtin_bit_cast(v8bf, sWab[(0 * 3 + tm) * NP * 64 + pp * 64 + lane]), acca, 0, 0, 0);
+            accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                h, __builtin_bit_cast(v8bf, sWab[(1 * 3 + tm) * NP * 64 + pp * 64 + lane]), accb, 0, 0, 0);
+          }
         }
-        // keep PF chunks (PF/2 pairs) of this step in flight
-        if (kc + PF < NKC) load_chunk(t, kc + PF);
         __builtin_amdgcn_sched_barrier(0);
       }
       // next round's first loads go out before this round's exchange and scan
