@@ -781,9 +781,10 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 }
 
 // Carry across the chunks of a chunked history, one thread per (sample,
-// state) entry of a (block, state group): from each chunk's summary
-// (G_c = product of its gates, X_c = its final state from 0; first and second
-// S plane of its first round) to the state it starts from,
+// state) entry of a (block, state group), a one-wave work-group per quarter
+// of the entries (so the summaries stream into many CUs at once): from each
+// chunk's summary (G_c = product of its gates, X_c = its final state from 0;
+// first and second S plane of its first round) to the state it starts from,
 //   x_start(0) = 0,  x_start(c+1) = G_c x_start(c) + X_c,
 // (second S plane) and the product of every later chunk's gates (first).
 // The summaries are read a batch of chunks at a time, every load of a batch
@@ -792,10 +793,14 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 // registers.
 constexpr int kCarryBatch = 64;
 
-__global__ __launch_bounds__(256) void fwd_carry_kernel(int NBG, int K, int L, int C, float* __restrict__ saved) {
-  const int bg = blockIdx.x;  // (block, state group)
+constexpr int kCarryThreads = 64;
+
+__global__ __launch_bounds__(kCarryThreads) void fwd_carry_kernel(int NBG, int K, int L, int C,
+                                                                  float* __restrict__ saved) {
+  constexpr int kParts = kPlane / kCarryThreads;
+  const int bg = blockIdx.x / kParts;  // (block, state group)
   if (bg >= NBG) return;
-  const int e = threadIdx.x;  // entry of the 16 x 16 plane
+  const int e = (blockIdx.x % kParts) * kCarryThreads + threadIdx.x;  // entry of the 16 x 16 plane
   float* sv = saved + (size_t)bg * saved_planes(K) * kPlane + e;
   const int rpc = L / kChunk;  // rounds per chunk
   auto gate = [&](int cc) { return sv + (size_t)(2 * K + 1 + cc * rpc) * kPlane; };
@@ -1668,7 +1673,8 @@ void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const
   }
   hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
                      hs2, WA, WB, WC, stab, ctx, saved, L, C, 1, nullptr, nullptr);
-  hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG), dim3(kPlane), 0, st, pl.NB * pl.NG, pl.K, L, C, saved);
+  hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG * (kPlane / kCarryThreads)), dim3(kCarryThreads), 0, st,
+                     pl.NB * pl.NG, pl.K, L, C, saved);
   hipLaunchKernelGGL((fwd_kernel<NKC, T, true>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
                      H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 2, tw, he);
 }
