@@ -103,6 +103,22 @@ __device__ __forceinline__ v4f ld4_in<float>(const float* p) {
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+// Two floats to two bf16 (round to nearest even) in one word, a's in the low half.
+__device__ __forceinline__ unsigned pk_bf16(float a, float b) {
+  typedef float v2f_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((v2f_t){a, b}, v2bf_t));
+}
+// Exact three-term bf16 split of two floats, packed: a = h + m + l (low
+// halves), b likewise (high halves), for |a|, |b| above ~1e-33.  Each
+// residual is exact in fp32 and has at most 16, then 8, significant bits.
+__device__ __forceinline__ void split3_pk(float a, float b, unsigned& h, unsigned& m, unsigned& l) {
+  h = pk_bf16(a, b);
+  const float ra = a - __uint_as_float(h << 16), rb = b - __uint_as_float(h & 0xffff0000u);
+  m = pk_bf16(ra, rb);
+  const float sa = ra - __uint_as_float(m << 16), sb = rb - __uint_as_float(m & 0xffff0000u);
+  l = pk_bf16(sa, sb);
+}
 __device__ __forceinline__ void ld8_bf16(const bf16_t* p, v4f& lo, v4f& hi) {
   const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
   lo[0] = __uint_as_float(w[0] << 16);
@@ -193,7 +209,22 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 #endif
   constexpr int PFP = PAIR ? (FWD_PAIR_PF < NKC / 2 ? FWD_PAIR_PF : NKC / 2) : 0;  // pairs in flight
   static_assert(!PAIR || PFP % 2 == 0, "bf16 loads go in spans of two pairs");
-  constexpr int PF = PAIR ? 2 * PFP : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC);   // chunks in flight
+  // fp32 history on the bf16 matrix cores (SPL): each history value x is
+  // split exactly into three bf16 terms as the weights w are (each term at
+  // most 2^-8 of the one before), and six of the nine term products enter
+  // the fp32 accumulator: the dropped mid*lo, lo*mid and lo*lo are below
+  // 2^-23 of x*w together, about one fp32 rounding.  Per 32 features six
+  // v_mfma_f32_16x16x32_bf16 replace eight v_mfma_f32_16x16x4_f32, about
+  // 37 % of their matrix-core cycles at the two peaks; the split's
+  // registers leave room for four loads in flight per wave.
+#ifndef FWD_SPLIT
+#define FWD_SPLIT 1
+#endif
+  constexpr bool SPL = FWD_SPLIT && !PAIR && !REPLAY;
+  constexpr int kSplitPrefetch = 4;
+  constexpr int PF = PAIR ? 2 * PFP
+                          : SPL ? (kSplitPrefetch < NKC ? kSplitPrefetch : NKC)
+                                : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC);  // chunks in flight
   static_assert(PAIR || PF % 2 == 0, "fp32 loads go in pairs");
   // bf16 trunk inputs feed bf16 MFMAs directly: each weight is split
   // exactly into three bf16 terms (hi + mid + lo == W for every fp32 W above
@@ -201,6 +232,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // rounds, as with fp32 MFMAs.  The readout keeps fp32 MFMAs on widened
   // h_s2.
   constexpr bool BFM = PAIR && !REPLAY;
+  constexpr bool WSPLIT = BFM || SPL;  // weights staged as three bf16 terms
   // History loads (CT): each load instruction covers 8 rows x 128 contiguous
   // bytes (lane (r8, p8): row r8 of one half of the block, 16 bytes at 16*p8
   // of a 128-byte span: 32 fp32 or 64 bf16 features), which streams ~10 %
@@ -210,17 +242,17 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // tiles).
   constexpr bool CT = !REPLAY;
   constexpr int NP = NKC / 2;  // 32-feature pairs of chunks
-  __shared__ v4f sWa[BFM ? 1 : NKC * 64];
-  __shared__ v4f sWb[BFM ? 1 : NKC * 64];
-  __shared__ v4u sWab[BFM ? 6 * NP * 64 : 1];  // [mat A|B][term hi|mid|lo][pair][lane]: 8 bf16
+  __shared__ v4f sWa[WSPLIT ? 1 : NKC * 64];
+  __shared__ v4f sWb[WSPLIT ? 1 : NKC * 64];
+  __shared__ v4u sWab[WSPLIT ? 6 * NP * 64 : 1];  // [mat A|B][term hi|mid|lo][pair][lane]: 8 bf16
   __shared__ v4f sWc[CT ? 1 : NKC * 64];
   __shared__ v4f sT[CT ? kFwdBlocks * kFwdWaves * 128 : 1];  // CT: [wave][half j][64 slots]
   __shared__ float sXa[kFwdBlocks][kChunk][kPlane];
   __shared__ float sXb[kFwdBlocks][kChunk][kPlane];
   // readout partials; with BFM they share sXa's memory (summed into c
   // before the first exchange writes it), which keeps two work-groups per CU
-  __shared__ float sCbuf[BFM ? 1 : kFwdBlocks * kFwdWaves * kPlane];
-  float(*sC)[kFwdWaves][kPlane] = BFM ? sXa : reinterpret_cast<float(*)[kFwdWaves][kPlane]>(sCbuf);
+  __shared__ float sCbuf[WSPLIT ? 1 : kFwdBlocks * kFwdWaves * kPlane];
+  float(*sC)[kFwdWaves][kPlane] = WSPLIT ? sXa : reinterpret_cast<float(*)[kFwdWaves][kPlane]>(sCbuf);
 
   const int D = NG * kGroup;
   const int xcd = blockIdx.x & 7;
@@ -279,7 +311,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // MFMA back.  Each thread loads rows of W_X[j][sg*16 + 4*s4 .. +3] as float4
   // and scatters them into the B-operand layout, where entry (kc, l) holds
   // W[kc*16 + 4*(l>>4) + i][sg*16 + (l&15)] for i = 0..3.
-  if constexpr (BFM) {
+  if constexpr (WSPLIT) {
     // W_A, W_B: a task is (matrix, octet o of rows 8o..8o+7, states
     // 4*s4..4*s4+3); per state n it writes the eight rows' three terms as
     // three 16-byte entries (pair o/4, lane (o%4, n)).
@@ -418,6 +450,9 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   const int wslot1 = 64 + 8 * r8 + (p8 ^ r8 ^ 1);
   const int rslot0 = 64 * (m >> 3) + 8 * (m & 7) + ((0 + kg) ^ (m & 7) ^ (m >> 3));
   const int rslot1 = 64 * (m >> 3) + 8 * (m & 7) + ((4 + kg) ^ (m & 7) ^ (m >> 3));
+  // SPL: operand lane (kg, m) reads row m's 32 bytes at 32*kg (slots 2kg and
+  // 2kg + 1, which differ in the last bit after the swizzle as well)
+  const int rslot8 = 64 * (m >> 3) + 8 * (m & 7) + ((2 * kg) ^ (m & 7) ^ (m >> 3));
   // REPLAY: this wave's step projections, as float4s of the alpha'/beta'
   // slots (its four samples 4kg+r at state m are entries kg*64 + 4m + r,
   // the MFMA result layout)
@@ -477,7 +512,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) sC[half][wave][(4 * kg + r) * kGroup + m] = acc[r];
   }
-  if constexpr (BFM) {
+  if constexpr (WSPLIT) {
     // sum the readout now: the partials' memory is sXa's
     __syncthreads();
     if (scanner) {
@@ -494,7 +529,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 #pragma unroll
   for (int i = 0; i < kRegRounds; ++i) Gr[i] = 1.f;
 
-  float gq[4] = {0.f, 0.f, 0.f, 0.f}, oq[4] = {0.f, 0.f, 0.f, 0.f};  // this wave's step: g, 1 - g
+  float gq[4] = {0.f, 0.f, 0.f, 0.f};  // this wave's step: m g (1 - g), for alpha'_t
   // Rounds r0 .. r1-1 of this chunk: at least one (a chunk is never empty),
   // written as do-while so the first round's loads above stay where they
   // are issued instead of moving into a loop-entry test.
@@ -547,6 +582,54 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       if (t + kChunk < t1) {
 #pragma unroll
         for (int kc = 0; kc < PF; kc += 2) load_chunk(t + kChunk, kc);
+      }
+      } else if constexpr (SPL) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        // the pair's two loads into this wave's tile, then back as this
+        // lane's eight consecutive features 32pp + 8kg .. +7 of row m
+        tile[wslot0] = hv[2 * pp];
+        tile[wslot1] = hv[2 * pp + 1];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // keep PF loads of this step in flight
+        if (2 * pp + PF < NKC) load_chunk(t, 2 * pp + PF);
+        if (2 * pp + 1 + PF < NKC) load_chunk(t, 2 * pp + 1 + PF);
+        v4u xw[3];  // the three terms, two bf16 per word
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const v4f x = tile[rslot8 ^ hf];
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            unsigned h, mm, l;
+            split3_pk(x[2 * w], x[2 * w + 1], h, mm, l);
+            xw[0][2 * hf + w] = h;
+            xw[1][2 * hf + w] = mm;
+            xw[2][2 * hf + w] = l;
+          }
+        }
+        v8bf xt[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) xt[k] = __builtin_bit_cast(v8bf, xw[k]);
+        // weight term tw with history terms ta <= 2 - tw, the smaller
+        // products first; one weight term's operands live at a time
+#pragma unroll
+        for (int tw = 2; tw >= 0; --tw) {
+          const v8bf wa = __builtin_bit_cast(v8bf, sWab[(0 * 3 + tw) * NP * 64 + pp * 64 + lane]);
+          const v8bf wb = __builtin_bit_cast(v8bf, sWab[(1 * 3 + tw) * NP * 64 + pp * 64 + lane]);
+#pragma unroll
+          for (int ta = 2 - tw; ta >= 0; --ta) {
+            acca = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xt[ta], wa, acca, 0, 0, 0);
+            accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xt[ta], wb, accb, 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // next round's first loads go out before this round's exchange and scan
+      if (t + kChunk < t1) {
+#pragma unroll
+        for (int kc = 0; kc < PF; ++kc) load_chunk(t + kChunk, kc);
       }
       } else if constexpr (CT) {
 #pragma unroll
@@ -613,14 +696,13 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       // computed without cancellation: e*g = e/(1+e) for a > 0.  The
       // stability multiplier m scales the gate and its derivative (m = 1
       // leaves every product bit-identical).  The exchange carries m*g and b;
-      // g and 1-g stay here for this step's alpha' below.
+      // m g (1 - g) stays here for this step's alpha' below.
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = acca[r];
         const float e = __expf(-a);
         const float g = __builtin_amdgcn_rcpf(1.f + e);
-        gq[r] = g;
-        oq[r] = a > 0.f ? e * g : 1.f - g;
+        gq[r] = g * (a > 0.f ? e * g : 1.f - g) * mstab;
         sXa[half][wave][(4 * kg + r) * kGroup + m] = g * mstab;
         sXb[half][wave][(4 * kg + r) * kGroup + m] = accb[r];
       }
@@ -629,7 +711,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 
     if (scanner) {
       const int idx = smp * kGroup + m;
-      if (!BFM && ch == r0) {
+      if (!WSPLIT && ch == r0) {
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kFwdWaves; ++w) s += sC[half][w][idx];
@@ -674,14 +756,12 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     __syncthreads();
     // Each projecting wave writes its step's planes: beta'_t and
     // alpha'_t = beta'_t * x_t * m g (1 - g), one float4 per lane (its four
-    // samples 4kg+r at state m are entries kg*64 + 4m + r of a plane); the
-    // summary pass of a chunked history writes the projections a_t and b_t
-    // there instead, for the second pass to replay.  The stores are
-    // unconditional; a descriptor of size 0 drops them for a wave past the
-    // chunk's last step, so no memory operation sits under a branch while the
-    // next round's loads are in flight.  (Every wave reads back only its own
-    // slots here, and writes them again only after its next projection, so
-    // no barrier is needed.)
+    // samples 4kg+r at state m are entries kg*64 + 4m + r of a plane).  The
+    // stores are unconditional; a descriptor of size 0 drops them for a wave
+    // past the chunk's last step (and in the summary pass), so no memory
+    // operation sits under a branch while the next round's loads are in
+    // flight.  (Every wave reads back only its own slots here, and writes
+    // them again only after its next projection, so no barrier is needed.)
     {
       const bool st_ok = t < t1 && blk_ok;
       const int ts = min(t, t1 - 1);
@@ -692,7 +772,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       for (int r = 0; r < 4; ++r) {
         const float xv = sXa[half][wave][(4 * kg + r) * kGroup + m];
         const float Pv = sXb[half][wave][(4 * kg + r) * kGroup + m];
-        al[r] = Pv * (xv * gq[r] * oq[r] * mstab);
+        al[r] = Pv * (xv * gq[r]);
         be[r] = Pv;
       }
       const unsigned off = (unsigned)(toff * sizeof(float));
