@@ -1494,6 +1494,7 @@ __device__ __forceinline__ const float* din_w_src(const float* WA, const float* 
 
 template <int NGT>
 struct DinW {
+  static constexpr bool kSplit = false;
   const float* sab;  // [jt][qq][lane] float4
   const float* sc;
   int lane;
@@ -1506,6 +1507,51 @@ struct DinW {
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t din_rsrc(float* base, unsigned bytes) { return make_rsrc(base, bytes); }
+
+// Split weights (D >= 32): the contraction runs on v_mfma_f32_16x16x32_bf16, K
+// chunk h covering kappa = 32h + 8kg + e (e = 0..7) for lane kg, with
+// kappa < D state kappa of W_A / d_a and kappa >= D state kappa - D of
+// W_B / d_b (the readout: W_C / d_c, zero past D).  Weights and d are split
+// exactly into three bf16 terms each and the six products with term
+// indices summing to at most 2 accumulate in fp32 (the dropped three are
+// below 2^-23 of the product together).
+#ifndef DIN_SPLIT
+#define DIN_SPLIT 1
+#endif
+template <int NGT>
+struct DinWs {
+  static constexpr bool kSplit = true;
+  static constexpr int NCS = NGT;                         // K chunks of a step unit (2D / 32)
+  static constexpr int NCR = (NGT * kGroup + 31) / 32;    // K chunks of a readout unit
+  // readout lanes kept: at D = 16 the lanes kg = 2, 3 of its one chunk
+  // carry kappa >= D, all zero, and are not stored
+  static constexpr int RL = NGT == 1 ? 32 : 64;
+  const v4u* ss;  // [jt][h][term][lane]
+  const v4u* sr;  // [jt][h][term][lane < RL]
+  int lane;
+  __device__ __forceinline__ v8bf S(int jt, int h, int tm) const {
+    return __builtin_bit_cast(v8bf, ss[((jt * NCS + h) * 3 + tm) * 64 + lane]);
+  }
+  __device__ __forceinline__ v8bf R(int jt, int h, int tm) const {
+    const v4u w = lane < RL ? sr[((jt * NCR + h) * 3 + tm) * RL + lane] : v4u{0u, 0u, 0u, 0u};
+    return __builtin_bit_cast(v8bf, w);
+  }
+};
+
+// Eight floats split exactly into three bf16 terms, as MFMA operands.
+__device__ __forceinline__ void split3_v8(const float (&v)[8], v8bf (&t)[3]) {
+  v4u w[3];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    unsigned h, mm, l;
+    split3_pk(v[2 * k], v[2 * k + 1], h, mm, l);
+    w[0][k] = h;
+    w[1][k] = mm;
+    w[2][k] = l;
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) t[k] = __builtin_bit_cast(v8bf, w[k]);
+}
 
 template <int NGT, bool ROUNDS, class WOps>
 __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const DinCtx& c, int SH2, int jb, int kg,
@@ -1531,6 +1577,41 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
     *reinterpret_cast<v4f*>(&tD[(g * 64 + lane) * 4]) = U.pd[g];
   }
   __builtin_amdgcn_wave_barrier();
+  v4f acc[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) acc[jt] = v4f{0.f, 0.f, 0.f, 0.f};
+  if constexpr (WOps::kSplit) {
+    // lane (kg, n): the eight d values of its K-chunk slots, sample n
+    constexpr int NCH = WOps::NCS;  // at least NCR
+    const int nch = readout ? WOps::NCR : WOps::NCS;
+#pragma unroll
+    for (int h = 0; h < NCH; ++h) {
+      if (h >= nch) break;  // uniform: the unit's kind
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kap = 32 * h + 8 * kg + e;
+        const int st = kap < D ? kap : kap - D;  // state
+        const int pidx = (st >> 4) * kDinPlaneLds + plane_index(n, st & 15);
+        float dc = tD[n * D + st];
+        if (ROUNDS && !readout) dc *= tS[pidx];
+        const float x = (readout || kap < D) ? tA[pidx] : tB[pidx];
+        v[e] = (readout && kap >= D) ? 0.f : dc * x;
+      }
+      v8bf dt[3];
+      split3_v8(v, dt);
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int tw = 2; tw >= 0; --tw) {
+          const v8bf w = readout ? W.R(jt, h, tw) : W.S(jt, h, tw);
+#pragma unroll
+          for (int td = 2 - tw; td >= 0; --td)
+            acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, dt[td], acc[jt], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+  } else {
   // B operands: lane (kg, n) at q-step i holds state 16(i/4) + 4kg + i%4 of
   // sample n (d_a for q-step i, d_b for q-step i + NQ)
   float da[NQ], db[NQ];
@@ -1545,9 +1626,6 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
   }
   __builtin_amdgcn_wave_barrier();
 
-  v4f acc[4];
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt) acc[jt] = v4f{0.f, 0.f, 0.f, 0.f};
   if (!readout) {
     // q-steps 0..NQ-1 contract d_a with W_A, NQ..2NQ-1 d_b with W_B
 #pragma unroll
@@ -1573,6 +1651,7 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
         for (int i = 0; i < 4; ++i) acc[jt] = mfma16x16x4(w[i], da[4 * qq + i], acc[jt]);
       }
     }
+  }
   }
   // Result lane (kg, n), element r: feature jt*16 + 4kg + r of the column
   // block, sample n.  Transposed through the tile so that lane (kg, n) then
@@ -1609,9 +1688,16 @@ __global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
     const float* __restrict__ saved, const float* __restrict__ dctx,
     float* __restrict__ dH, float* __restrict__ dhs2) {
   constexpr int D = NGT * kGroup;
-  // weights: [tile jt][q-step group qq][lane] float4
-  __shared__ float sWab[4 * 2 * NGT * 64 * 4];
-  __shared__ float sWc[4 * NGT * 64 * 4];
+  // weights: [tile jt][q-step group qq][lane] float4, or (split) three bf16
+  // terms per [tile jt][K chunk h][lane]
+  // split weights pay from two state groups on (at D = 16 the per-unit
+  // split of d and the larger weight tile cost more than the MFMAs saved)
+  constexpr bool SPLIT = DIN_SPLIT && NGT >= 2;
+  using WS = DinWs<NGT>;
+  __shared__ float sWab[SPLIT ? 4 : 4 * 2 * NGT * 64 * 4];
+  __shared__ float sWc[SPLIT ? 4 : 4 * NGT * 64 * 4];
+  __shared__ v4u sWs[SPLIT ? 4 * WS::NCS * 3 * 64 : 1];
+  __shared__ v4u sWr[SPLIT ? 4 * WS::NCR * 3 * WS::RL : 1];
   __shared__ float sTile[kDinWaves][din_tile_floats(NGT)];
 
   const int NJB = SH2 / kColBlock;
@@ -1641,19 +1727,57 @@ __global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
   DinUnit<NGT> R0, R1;
   din_load<NGT, ROUNDS>(R0, min(wave, n_units - 1), c, lane);
 
-  for (int e = tid; e < 4 * 2 * NGT * 64; e += kDinWaves * 64) {
-    const int l = e & 63, qq = (e >> 6) % (2 * NGT), jt = (e >> 6) / (2 * NGT);
-    const size_t row = (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * D + 4 * (l >> 4);
-    *reinterpret_cast<v4f*>(&sWab[e * 4]) = ld4(din_w_src(WA, WB, NGT, qq) + row + 16 * (qq % NGT));
+  if constexpr (SPLIT) {
+    // lane l of (tile jt, chunk h): feature row jb*64 + jt*16 + l%16, the
+    // eight weights of kappa = 32h + 8(l/16) .. +7 (W_A below D, W_B above;
+    // W_C below D and zeros above for the readout), three terms each
+    for (int e = tid; e < 4 * WS::NCS * 64 + 4 * WS::NCR * WS::RL; e += kDinWaves * 64) {
+      const bool ro = e >= 4 * WS::NCS * 64;
+      const int ee = ro ? e - 4 * WS::NCS * 64 : e;
+      const int nc = ro ? WS::NCR : WS::NCS;
+      const int nl = ro ? WS::RL : 64;
+      const int l = ee % nl, h = (ee / nl) % nc, jt = (ee / nl) / nc;
+      const size_t row = (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * D;
+      const int k0 = 32 * h + 8 * (l >> 4);
+      float v[8];
+      if (ro && k0 >= D) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = 0.f;
+      } else {
+        const float* src = ro ? WC + row + k0 : (k0 < D ? WA + row + k0 : WB + row + (k0 - D));
+        const v4f a = ld4(src), b = ld4(src + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[k] = a[k];
+          v[4 + k] = b[k];
+        }
+      }
+      v8bf tw[3];
+      split3_v8(v, tw);
+      v4u* dst = ro ? sWr : sWs;
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm) dst[((jt * nc + h) * 3 + tm) * nl + l] = __builtin_bit_cast(v4u, tw[tm]);
+    }
+  } else {
+    for (int e = tid; e < 4 * 2 * NGT * 64; e += kDinWaves * 64) {
+      const int l = e & 63, qq = (e >> 6) % (2 * NGT), jt = (e >> 6) / (2 * NGT);
+      const size_t row = (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * D + 4 * (l >> 4);
+      *reinterpret_cast<v4f*>(&sWab[e * 4]) = ld4(din_w_src(WA, WB, NGT, qq) + row + 16 * (qq % NGT));
+    }
+    for (int e = tid; e < 4 * NGT * 64; e += kDinWaves * 64) {
+      const int l = e & 63, qq = (e >> 6) % NGT, jt = (e >> 6) / NGT;
+      const size_t row = (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * D + 4 * (l >> 4);
+      *reinterpret_cast<v4f*>(&sWc[e * 4]) = ld4(WC + row + 16 * qq);
+    }
   }
-  for (int e = tid; e < 4 * NGT * 64; e += kDinWaves * 64) {
-    const int l = e & 63, qq = (e >> 6) % NGT, jt = (e >> 6) / NGT;
-    const size_t row = (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * D + 4 * (l >> 4);
-    *reinterpret_cast<v4f*>(&sWc[e * 4]) = ld4(WC + row + 16 * qq);
+  std::conditional_t<SPLIT, DinWs<NGT>, DinW<NGT>> W;
+  if constexpr (SPLIT) {
+    W.ss = sWs;
+    W.sr = sWr;
+  } else {
+    W.sab = sWab;
+    W.sc = sWc;
   }
-  DinW<NGT> W;
-  W.sab = sWab;
-  W.sc = sWc;
   W.lane = lane;
   __syncthreads();
 

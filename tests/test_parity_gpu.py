@@ -98,6 +98,7 @@ EDGE_SHAPES = [
     (300, 12, 256, 16),
     (20, 80, 64, 16),     # ten 8-step rounds: two beyond those held in registers
     (5, 100, 128, 32),
+    (7, 20, 128, 64),     # four state groups over three rounds
 ]
 
 
@@ -313,8 +314,8 @@ FP32_CLASS_OUT = 5e-6
 FP32_CLASS_DW = 3e-6
 
 
-@pytest.mark.parametrize("shape", [(300, 8, 256, 16), (300, 64, 256, 16), (64, 8, 512, 64)],
-                         ids=["K8", "K64", "wide"])
+@pytest.mark.parametrize("shape", [(300, 8, 256, 16), (300, 64, 256, 16), (64, 8, 512, 64), (40, 20, 192, 32)],
+                         ids=["K8", "K64", "wide", "D32_rounds"])
 def test_fp32_class_accuracy(shape):
     B, K, SH2, D = shape
     inp = make_inputs(B, K, SH2, D, seed=7)
@@ -329,3 +330,13 @@ def test_fp32_class_accuracy(shape):
         ref = getattr(b, name)
         rel = float(np.sum(np.abs(np.asarray(out[name], np.float64) - ref)) / np.sum(np.abs(ref)))
         assert rel <= FP32_CLASS_DW, f"{name}: {rel:.3e}"
+    # input gradients (bf16 split terms from D = 32 on, fp32 MFMAs at D = 16)
+    t = _to_dev(inp)
+    _, saved = m2.fwd(t["h_history"], t["h_s2"], t["W_A"], t["W_B"], t["W_C"])
+    dH, dhs2 = m2.bwd_input(t["W_A"], t["W_B"], t["W_C"], saved, t["d_context"], K)
+    torch.cuda.synchronize()
+    ig = orc.input_grads(b, inp["W_A"], inp["W_B"], inp["W_C"])
+    for name, gpu, ref in (("d_h_history", dH, ig.d_h_history), ("d_h_s2", dhs2, ig.d_h_s2)):
+        gpu = gpu.cpu().numpy().astype(np.float64)
+        worst = float(np.max(np.abs(gpu - ref) / (1.0 + np.abs(ref))))
+        assert worst <= FP32_CLASS_OUT, f"{name}: {worst:.3e}"
