@@ -1027,23 +1027,23 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, 
 // exactly into three bf16 terms, so every product is exact and only the
 // fp32 accumulation rounds.
 __device__ __forceinline__ void bf16_split3(const float (&d)[4], v4bf (&t)[3]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const __bf16 hi = (__bf16)d[i];
-    const float r1 = d[i] - (float)hi;
-    const __bf16 mi = (__bf16)r1;
-    t[0][i] = hi;
-    t[1][i] = mi;
-    t[2][i] = (__bf16)(r1 - (float)mi);
-  }
+  unsigned h0, m0, l0, h1, m1, l1;
+  split3_pk(d[0], d[1], h0, m0, l0);
+  split3_pk(d[2], d[3], h1, m1, l1);
+  t[0] = __builtin_bit_cast(v4bf, v2u{h0, h1});
+  t[1] = __builtin_bit_cast(v4bf, v2u{m0, m1});
+  t[2] = __builtin_bit_cast(v4bf, v2u{l0, l1});
 }
 __device__ __forceinline__ void bf16_tiles(const BwdUnit& U, v4bf (&a)[4]) {
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
-    const int w = qq >> 1, sh = (qq & 1) * 16;
+    // the low (qq even) or high (qq odd) halves of two rows' words, row 0's
+    // in the low half of the result (one byte permute)
+    const int w = qq >> 1;
+    const unsigned sel = (qq & 1) ? 0x07060302u : 0x05040100u;
     v2u p;
-    p[0] = ((U.hr[0][w] >> sh) & 0xffffu) | (((U.hr[1][w] >> sh) & 0xffffu) << 16);
-    p[1] = ((U.hr[2][w] >> sh) & 0xffffu) | (((U.hr[3][w] >> sh) & 0xffffu) << 16);
+    p[0] = __builtin_amdgcn_perm(U.hr[1][w], U.hr[0][w], sel);
+    p[1] = __builtin_amdgcn_perm(U.hr[3][w], U.hr[2][w], sel);
     a[qq] = __builtin_bit_cast(v4bf, p);
   }
 }
