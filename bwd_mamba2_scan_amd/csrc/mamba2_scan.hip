@@ -174,10 +174,13 @@ __host__ __device__ __forceinline__ int saved_planes(int K) {
 
 // ---------------------------------------------------------------------------
 // Forward.
-//   grid  = 8 * NG * ceil(NB / 8) work-groups, 512 threads each.
+//   grid  = 8 * NG * ceil(pairs * C / 8) work-groups (pairs: groups of one or
+//   two sample blocks, C history chunks), 512 or 1024 threads each.
 //   LDS   = 3 * SH2 * 16 * 4 B (weights) + 16 KiB (a|b exchange) + 8 KiB (c).
 // Work-group w runs on XCD w % 8; the NG state groups of one sample block are
-// given consecutive rounds on the same XCD so their h_history reads share L2.
+// given consecutive rounds on the same XCD so their h_history reads share L2,
+// and the chunks of a chunked history spread over the XCDs even when there
+// are fewer sample blocks than XCDs.
 //
 // The weight slab is staged before any history load is issued (the vector
 // memory pipe returns data in issue order, so slab loads queued behind the
@@ -258,8 +261,11 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   const int xcd = blockIdx.x & 7;
   const int round = blockIdx.x >> 3;
   const int sg = round % NG;
-  const int cidx = (round / NG) % C;  // history chunk of this work-group (C = 1: the whole history)
-  const int pair = (round / NG / C) * 8 + xcd;  // this work-group's sample blocks
+  // (sample blocks, history chunk) items go round-robin over the XCDs, the
+  // chunks of one item's blocks on consecutive XCDs (C = 1: the whole history)
+  const int item = (round / NG) * 8 + xcd;
+  const int cidx = item % C;   // history chunk of this work-group
+  const int pair = item / C;   // this work-group's sample blocks
   if (pair * kFwdBlocks >= NB) return;
   // steps [t0, t1) of this chunk: rounds r0 .. r1-1 (a round is kChunk steps)
   const int t0 = cidx * L;
@@ -860,69 +866,83 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   }
 }
 
-// Carry across the chunks of a chunked history, one thread per (sample,
-// state) entry of a (block, state group), a one-wave work-group per quarter
-// of the entries (so the summaries stream into many CUs at once): from each
-// chunk's summary (G_c = product of its gates, X_c = its final state from 0;
-// first and second S plane of its first round) to the state it starts from,
+// Carry across the chunks of a chunked history, per (sample, state) entry
+// of a (block, state group): from each chunk's summary (G_c = product of its
+// gates, X_c = its final state from 0; first and second S plane of its first
+// round) to the state it starts from,
 //   x_start(0) = 0,  x_start(c+1) = G_c x_start(c) + X_c,
 // (second S plane) and the product of every later chunk's gates (first).
-// The summaries are read a batch of chunks at a time, every load of a batch
-// in flight together (the recurrence itself is a few FMAs per chunk); with
-// at most one batch of chunks, the suffix products reuse the gates in
-// registers.
-constexpr int kCarryBatch = 64;
+// The chunks of an entry are cut into T segments of at most kCarrySeg
+// consecutive chunks, one thread each, all of a segment's summaries loaded
+// at once.  A segment composes to one affine map (product of its gates, its
+// state from 0); each thread then composes the maps of the segments before
+// its own (from LDS) for its start state and multiplies the gate products of
+// the segments after it, and walks its chunks once forward and once back.
+// Work-group (bg, part): 256 threads, entries part*256/T .. +256/T - 1 of
+// (block, state group) bg, T segments each (T a power of two, <= 32).
+constexpr int kCarrySeg = 16;
+constexpr int kCarryThreads = 256;
 
-constexpr int kCarryThreads = 64;
+static_assert(kFwdChunkTarget / kCarrySeg <= kCarryThreads, "carry segments per entry fit a work-group");
 
-__global__ __launch_bounds__(kCarryThreads) void fwd_carry_kernel(int NBG, int K, int L, int C,
+int carry_segments(int C) {
+  int t = 1;
+  while (t * kCarrySeg < C) t *= 2;
+  return t;
+}
+
+__global__ __launch_bounds__(kCarryThreads) void fwd_carry_kernel(int NBG, int K, int L, int C, int T,
                                                                   float* __restrict__ saved) {
-  constexpr int kParts = kPlane / kCarryThreads;
-  const int bg = blockIdx.x / kParts;  // (block, state group)
+  __shared__ float sG[kCarryThreads], sX[kCarryThreads];  // [segment][entry of the work-group]
+  const int epg = kCarryThreads / T;  // entries per work-group
+  const int bg = blockIdx.x / T;      // (block, state group)
   if (bg >= NBG) return;
-  const int e = (blockIdx.x % kParts) * kCarryThreads + threadIdx.x;  // entry of the 16 x 16 plane
+  const int j = threadIdx.x / epg;    // segment
+  const int el = threadIdx.x % epg;
+  const int e = (blockIdx.x % T) * epg + el;  // entry of the 16 x 16 plane
   float* sv = saved + (size_t)bg * saved_planes(K) * kPlane + e;
   const int rpc = L / kChunk;  // rounds per chunk
   auto gate = [&](int cc) { return sv + (size_t)(2 * K + 1 + cc * rpc) * kPlane; };
   auto state = [&](int cc) { return sv + (size_t)(2 * K + 2 + cc * rpc) * kPlane; };
-  float G[kCarryBatch];
-  float x = 0.f;
-  for (int c0 = 0; c0 < C; c0 += kCarryBatch) {
-    float X[kCarryBatch];
+  const int M = (C + T - 1) / T;  // chunks per segment, <= kCarrySeg
+  const int c0 = j * M;
+  const int n = max(0, min(C, c0 + M) - c0);  // this segment's chunks (the last may be short or empty)
+  float G[kCarrySeg], X[kCarrySeg];
 #pragma unroll
-    for (int i = 0; i < kCarryBatch; ++i) {  // clamped: every load unconditional
-      const int cc = min(c0 + i, C - 1);
-      G[i] = *gate(cc);
-      X[i] = *state(cc);
-    }
+  for (int i = 0; i < kCarrySeg; ++i) {  // clamped: every load unconditional
+    const int cc = min(c0 + min(i, n - 1), C - 1);
+    G[i] = *gate(max(cc, 0));
+    X[i] = *state(max(cc, 0));
+  }
+  float gs = 1.f, xs = 0.f;  // the segment's map: x -> gs x + xs
 #pragma unroll
-    for (int i = 0; i < kCarryBatch; ++i) {
-      if (c0 + i < C) {
-        *state(c0 + i) = x;
-        x = G[i] * x + X[i];
-      }
+  for (int i = 0; i < kCarrySeg; ++i) {
+    if (i < n) {
+      xs = G[i] * xs + X[i];
+      gs *= G[i];
     }
   }
-  float S = 1.f;
-  if (C <= kCarryBatch) {
-#pragma unroll
-    for (int i = kCarryBatch - 1; i >= 0; --i) {
-      if (i < C) {
-        *gate(i) = S;
-        S *= G[i];
-      }
-    }
-    return;
+  sG[threadIdx.x] = gs;
+  sX[threadIdx.x] = xs;
+  __syncthreads();
+  float x = 0.f, S = 1.f;
+  for (int jj = 0; jj < T; ++jj) {
+    const float g = sG[jj * epg + el], xx = sX[jj * epg + el];
+    if (jj < j) x = g * x + xx;
+    if (jj > j) S *= g;
   }
-  for (int c1 = C; c1 > 0; c1 -= kCarryBatch) {
 #pragma unroll
-    for (int i = 0; i < kCarryBatch; ++i) G[i] = *gate(max(c1 - 1 - i, 0));
+  for (int i = 0; i < kCarrySeg; ++i) {
+    if (i < n) {
+      *state(c0 + i) = x;
+      x = G[i] * x + X[i];
+    }
+  }
 #pragma unroll
-    for (int i = 0; i < kCarryBatch; ++i) {
-      if (c1 - 1 - i >= 0) {
-        *gate(c1 - 1 - i) = S;
-        S *= G[i];
-      }
+  for (int i = kCarrySeg - 1; i >= 0; --i) {
+    if (i < n) {
+      *gate(c0 + i) = S;
+      S *= G[i];
     }
   }
 }
@@ -1869,7 +1889,7 @@ void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const
   constexpr int kFwdBlocks = fwd_blocks(NKC);
   constexpr int kFwdThreads = fwd_threads(NKC);
   const int pairs = (pl.NB + kFwdBlocks - 1) / kFwdBlocks;
-  const int grid = 8 * pl.NG * C * ((pairs + 7) / 8);
+  const int grid = 8 * pl.NG * ((pairs * C + 7) / 8);
   if (C == 1) {
     hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
                        H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 0, tw, he);
@@ -1877,8 +1897,9 @@ void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const
   }
   hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
                      hs2, WA, WB, WC, stab, ctx, saved, L, C, 1, nullptr, nullptr);
-  hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG * (kPlane / kCarryThreads)), dim3(kCarryThreads), 0, st,
-                     pl.NB * pl.NG, pl.K, L, C, saved);
+  const int nseg = carry_segments(C);  // C <= kFwdChunkTarget, so nseg <= kFwdChunkTarget / kCarrySeg
+  hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG * nseg), dim3(kCarryThreads), 0, st, pl.NB * pl.NG, pl.K,
+                     L, C, nseg, saved);
   hipLaunchKernelGGL((fwd_kernel<NKC, T, true>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
                      H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 2, tw, he);
 }

@@ -272,6 +272,7 @@ LONG_FEW_SHAPES = [
     (8, 2048, 128, 32),
     (3, 300, 64, 64),
     (17, 160, 192, 16),
+    (5, 8192, 64, 16),    # one sample block: 512 history chunks, the carry's 32 segments
 ]
 
 
