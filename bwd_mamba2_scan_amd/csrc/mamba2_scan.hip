@@ -63,7 +63,7 @@ constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
 // CU, which measured faster there).
 __host__ __device__ constexpr int fwd_blocks(int nkc) { return nkc >= 20 ? 2 : 1; }
 __host__ __device__ constexpr int fwd_threads(int nkc) { return fwd_blocks(nkc) * kFwdWaves * 64; }
-constexpr int kFwdPrefetch = 6;    // history loads each forward wave keeps in flight
+constexpr int kFwdPrefetch = 4;    // fp32 history loads each forward wave keeps in flight
 constexpr int kRegRounds = 8;      // rounds whose gate product the forward keeps in registers
 constexpr int kFwdChunkTarget = 512;  // forward work-groups a chunked history aims for
 constexpr int kBwdWaves = 12;
@@ -220,14 +220,8 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // v_mfma_f32_16x16x32_bf16 replace eight v_mfma_f32_16x16x4_f32, about
   // 37 % of their matrix-core cycles at the two peaks; the split's
   // registers leave room for four loads in flight per wave.
-#ifndef FWD_SPLIT
-#define FWD_SPLIT 1
-#endif
-  constexpr bool SPL = FWD_SPLIT && !PAIR && !REPLAY;
-  constexpr int kSplitPrefetch = 4;
-  constexpr int PF = PAIR ? 2 * PFP
-                          : SPL ? (kSplitPrefetch < NKC ? kSplitPrefetch : NKC)
-                                : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC);  // chunks in flight
+  constexpr bool SPL = !PAIR && !REPLAY;
+  constexpr int PF = PAIR ? 2 * PFP : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC);  // chunks in flight
   static_assert(PAIR || PF % 2 == 0, "fp32 loads go in pairs");
   // bf16 trunk inputs feed bf16 MFMAs directly: each weight is split
   // exactly into three bf16 terms (hi + mid + lo == W for every fp32 W above
@@ -245,8 +239,6 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // tiles).
   constexpr bool CT = !REPLAY;
   constexpr int NP = NKC / 2;  // 32-feature pairs of chunks
-  __shared__ v4f sWa[WSPLIT ? 1 : NKC * 64];
-  __shared__ v4f sWb[WSPLIT ? 1 : NKC * 64];
   __shared__ v4u sWab[WSPLIT ? 6 * NP * 64 : 1];  // [mat A|B][term hi|mid|lo][pair][lane]: 8 bf16
   __shared__ v4f sWc[CT ? 1 : NKC * 64];
   __shared__ v4f sT[CT ? kFwdBlocks * kFwdWaves * 128 : 1];  // CT: [wave][half j][64 slots]
@@ -314,9 +306,11 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 
   // (1) Weight slab, staged before any history load is issued: the slab's
   // loads would otherwise queue behind the CU's history stream and hold every
-  // MFMA back.  Each thread loads rows of W_X[j][sg*16 + 4*s4 .. +3] as float4
-  // and scatters them into the B-operand layout, where entry (kc, l) holds
-  // W[kc*16 + 4*(l>>4) + i][sg*16 + (l&15)] for i = 0..3.
+  // MFMA back.  W_A and W_B go in as three bf16 terms each, in the
+  // v_mfma_f32_16x16x32_bf16 B-operand layout; the replay pass stages only
+  // W_C, in fp32 for the readout, where entry (kc, l) holds
+  // W[kc*16 + 4*(l>>4) + i][sg*16 + (l&15)] for i = 0..3 (pair order for
+  // bf16 inputs).
   if constexpr (WSPLIT) {
     // W_A, W_B: a task is (matrix, octet o of rows 8o..8o+7, states
     // 4*s4..4*s4+3); per state n it writes the eight rows' three terms as
@@ -353,27 +347,21 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       }
     }
   } else {
-    constexpr int NW4 = SH2 * 4;  // float4s per matrix slab
-    constexpr int NMAT = REPLAY ? 1 : (CT ? 2 : 3);  // REPLAY: W_C only; CT: W_A, W_B
-    constexpr int M0 = REPLAY ? 2 : 0;
-    constexpr int NWT = (NMAT * NW4 + kFwdThreads - 1) / kFwdThreads;
+    // REPLAY: only W_C, for the readout
+    constexpr int NW4 = SH2 * 4;  // float4s of the slab
+    constexpr int NWT = (NW4 + kFwdThreads - 1) / kFwdThreads;
     v4f wr[NWT];
 #pragma unroll
     for (int it = 0; it < NWT; ++it) {
-      const int f = tid + it * kFwdThreads;
-      if (f < NMAT * NW4) {
-        const int mat = M0 + f / NW4, r = f - (mat - M0) * NW4;
-        const float* W = mat == 0 ? WA : (mat == 1 ? WB : WC);
-        wr[it] = ld4(W + (size_t)(r >> 2) * D + sg * kGroup + 4 * (r & 3));
-      }
+      const int r = tid + it * kFwdThreads;
+      if (r < NW4) wr[it] = ld4(WC + (size_t)(r >> 2) * D + sg * kGroup + 4 * (r & 3));
     }
 #pragma unroll
     for (int it = 0; it < NWT; ++it) {
-      const int f = tid + it * kFwdThreads;
-      if (f < NMAT * NW4) {
-        const int mat = M0 + f / NW4, r = f - (mat - M0) * NW4;
+      const int r = tid + it * kFwdThreads;
+      if (r < NW4) {
         const int j = r >> 2, s4 = r & 3;
-        float* dst = reinterpret_cast<float*>(mat == 0 ? sWa : (mat == 1 ? sWb : sWc));
+        float* dst = reinterpret_cast<float*>(sWc);
         // feature j -> (chunk, k-group, element) of the A/B operand order
         const int jc = PAIR ? 2 * (j >> 5) + ((j & 7) >> 2) : (j >> 4);
         const int jg = PAIR ? ((j & 31) >> 3) : ((j >> 2) & 3);
@@ -427,7 +415,6 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       for (int i = 0; i < 4; ++i) wcv[r][i] = WC[(size_t)(kc * 16 + 4 * kg + i) * D + sg * kGroup + m];
     }
   }
-  const T* hbase = H + (size_t)smp_a * K * SH2 + koff;
   // CT: lane (r8, p8) loads rows r8 and 8 + r8 of the block
   const int r8 = lane >> 3, p8 = lane & 7;
   const T* hb0 = H + (size_t)min(blk * kBlock + r8, B - 1) * K * SH2 + (16 / sizeof(T)) * p8;
@@ -439,12 +426,8 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     if constexpr (BFM)  // load kc/2: half (kc/2) & 1 of the 64-feature span kc/4
       hr[kc >> 1] = __builtin_nontemporal_load(
           reinterpret_cast<const v4u*>((((kc >> 1) & 1) ? hb1 : hb0) + (size_t)t * SH2 + (kc >> 2) * 64));
-    else if constexpr (PAIR)
-      ld8_bf16(hbase + (size_t)t * SH2 + (kc >> 1) * 32, hv[kc], hv[kc + 1]);
-    else if constexpr (CT)  // load kc: half kc & 1 of pair kc >> 1
+    else  // fp32, load kc: half kc & 1 of pair kc >> 1
       hv[kc] = ld4_in(((kc & 1) ? hb1 : hb0) + (size_t)t * SH2 + (kc >> 1) * 32);
-    else
-      hv[kc] = ld4_in(hbase + (size_t)t * SH2 + kc * 16);
   };
   // CT tile slots (16 bytes each), XOR-swizzled so that the writes of 8
   // lanes and the operand reads of 16 lanes each touch distinct banks: lane
@@ -456,8 +439,8 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   const int wslot1 = 64 + 8 * r8 + (p8 ^ r8 ^ 1);
   const int rslot0 = 64 * (m >> 3) + 8 * (m & 7) + ((0 + kg) ^ (m & 7) ^ (m >> 3));
   const int rslot1 = 64 * (m >> 3) + 8 * (m & 7) + ((4 + kg) ^ (m & 7) ^ (m >> 3));
-  // SPL: operand lane (kg, m) reads row m's 32 bytes at 32*kg (slots 2kg and
-  // 2kg + 1, which differ in the last bit after the swizzle as well)
+  // fp32: operand lane (kg, m) reads row m's 32 bytes at 32*kg (slots 2kg
+  // and 2kg + 1, which differ in the last bit after the swizzle as well)
   const int rslot8 = 64 * (m >> 3) + 8 * (m & 7) + ((2 * kg) ^ (m & 7) ^ (m >> 3));
   // REPLAY: this wave's step projections, as float4s of the alpha'/beta'
   // slots (its four samples 4kg+r at state m are entries kg*64 + 4m + r,
@@ -589,7 +572,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
 #pragma unroll
         for (int kc = 0; kc < PF; kc += 2) load_chunk(t + kChunk, kc);
       }
-      } else if constexpr (SPL) {
+      } else {  // fp32 history, split into bf16 terms
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp) {
         // the pair's two loads into this wave's tile, then back as this
@@ -636,61 +619,6 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       if (t + kChunk < t1) {
 #pragma unroll
         for (int kc = 0; kc < PF; ++kc) load_chunk(t + kChunk, kc);
-      }
-      } else if constexpr (CT) {
-#pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        // the pair's two loads into this wave's tile, then back in operand order
-        tile[wslot0] = hv[2 * pp];
-        tile[wslot1] = hv[2 * pp + 1];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const v4f a0 = tile[rslot0];
-        const v4f a1 = tile[rslot1];
-        // keep PF loads of this step in flight
-        if (2 * pp + PF < NKC) load_chunk(t, 2 * pp + PF);
-        if (2 * pp + 1 + PF < NKC) load_chunk(t, 2 * pp + 1 + PF);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const v4f av = h ? a1 : a0;
-          const v4f wa = sWa[(2 * pp + h) * 64 + lane];
-          const v4f wb = sWb[(2 * pp + h) * 64 + lane];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acca = mfma16x16x4(av[i], wa[i], acca);
-            accb = mfma16x16x4(av[i], wb[i], accb);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // next round's first loads go out before this round's exchange and scan
-      if (t + kChunk < t1) {
-#pragma unroll
-        for (int kc = 0; kc < PF; ++kc) load_chunk(t + kChunk, kc);
-      }
-      } else {
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const v4f wa = sWa[kc * 64 + lane];
-        const v4f wb = sWb[kc * 64 + lane];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acca = mfma16x16x4(hv[kc][i], wa[i], acca);
-          accb = mfma16x16x4(hv[kc][i], wb[i], accb);
-        }
-        // keep PF chunks of this step in flight (pairs: after a pair's second chunk)
-        if constexpr (PAIR) {
-          if ((kc & 1) && kc + 1 + PF - 2 < NKC - 1 && kc + PF < NKC) load_chunk(t, kc + PF - 1);
-        } else {
-          if (kc + PF < NKC) load_chunk(t, kc + PF);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // next round's first loads go out before this round's exchange and scan
-      if (t + kChunk < t1) {
-#pragma unroll
-        for (int kc = 0; kc < PF; kc += PAIR ? 2 : 1) load_chunk(t + kChunk, kc);
       }
       }
       sa = acca;
@@ -1535,9 +1463,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t din_rsrc(float* base, unsigned
 // exactly into three bf16 terms each and the six products with term
 // indices summing to at most 2 accumulate in fp32 (the dropped three are
 // below 2^-23 of the product together).
-#ifndef DIN_SPLIT
-#define DIN_SPLIT 1
-#endif
 template <int NGT>
 struct DinWs {
   static constexpr bool kSplit = true;
@@ -1712,7 +1637,7 @@ __global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
   // terms per [tile jt][K chunk h][lane]
   // split weights pay from two state groups on (at D = 16 the per-unit
   // split of d and the larger weight tile cost more than the MFMAs saved)
-  constexpr bool SPLIT = DIN_SPLIT && NGT >= 2;
+  constexpr bool SPLIT = NGT >= 2;
   using WS = DinWs<NGT>;
   __shared__ float sWab[SPLIT ? 4 : 4 * 2 * NGT * 64 * 4];
   __shared__ float sWc[SPLIT ? 4 : 4 * NGT * 64 * 4];
