@@ -10,13 +10,17 @@
 // Design (the pages' cuBLAS-plus-scan split is prior art, not followed):
 //
 //  * fwd_kernel: one work-group per (block of 16 samples, group of 16 states).
-//    The [W_A | W_B | W_C] slab of the state group sits in LDS in the fp32
-//    MFMA B-operand layout.  Each of the 8 waves projects one history step of
-//    the 16 samples with v_mfma_f32_16x16x4_f32 (M = samples, N = states,
-//    K = trunk features), streaming every h_history row from HBM once.  The
-//    a|b tiles meet in LDS, where 4 waves run the recurrence, one lane per
-//    (sample, state), in registers.  The readout c is split over the waves by
-//    trunk chunk and summed in a fixed order.
+//    W_A and W_B of the state group sit in LDS, each weight split exactly
+//    into three bf16 terms, in the v_mfma_f32_16x16x32_bf16 B-operand layout.
+//    Each of the 8 waves projects one history step of the 16 samples
+//    (M = samples, N = states, K = trunk features), streaming every
+//    h_history row from HBM once as 8 rows x 128 B per load, through a
+//    per-wave LDS tile into the operand order, where each value is split
+//    into three bf16 terms too; six of the nine term products accumulate in
+//    fp32.  The a|b tiles meet in LDS, where 4 waves run the recurrence, one
+//    lane per (sample, state), in registers.  The readout c (fp32 MFMAs, W_C
+//    read from memory) is split over the waves by trunk chunk and summed in
+//    a fixed order.
 //
 //  * The backward needs no sequential scan.  With P_t = prod_{v>t} g_v,
 //      d_b_t = d_context * (c P_t),   d_a_t = d_context * (c P_t x_t g_t (1-g_t)),
@@ -176,7 +180,8 @@ __host__ __device__ __forceinline__ int saved_planes(int K) {
 // Forward.
 //   grid  = 8 * NG * ceil(pairs * C / 8) work-groups (pairs: groups of one or
 //   two sample blocks, C history chunks), 512 or 1024 threads each.
-//   LDS   = 3 * SH2 * 16 * 4 B (weights) + 16 KiB (a|b exchange) + 8 KiB (c).
+//   LDS   = 2 * SH2 * 16 * 3 * 2 B (weight terms) + 16 KiB (a|b exchange, also
+//   the readout partials) + 2 KiB per wave (load tiles), per sample block.
 // Work-group w runs on XCD w % 8; the NG state groups of one sample block are
 // given consecutive rounds on the same XCD so their h_history reads share L2,
 // and the chunks of a chunked history spread over the XCDs even when there
