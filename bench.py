@@ -1,6 +1,6 @@
 """Benchmark: ms per Mamba2 scan fwd+bwd step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload pages_shape] [--no-extras]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 16] [--workload pages_shape] [--no-extras]
 
 One step = mamba2_scan_fwd + mamba2_scan_bwd (partials + reduce) over one
 batch of seeded synthetic input already resident in HBM.  Prints one JSON line.
@@ -175,8 +175,8 @@ def parity_gate(m2, torch, t, inputs):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="pages_shape")
     ap.add_argument("--sets", type=int, default=8, help="rotating input sets (even, >= 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
