@@ -1319,26 +1319,40 @@ __global__ __launch_bounds__(kBlendWaves * 64) void blend_bwd_kernel(
   }
   const int b0 = p * RPW;
   const int b1 = min(B, b0 + RPW);
-  for (int b = b0 + wave; b < b1; b += kBlendWaves) {
-    v4f dv[2];
-    float part = 0.f;
+  // A wave's rows come kBlendRows at a time, every load of the batch issued
+  // before the first is used (a row's own work is two wave sums); a row past
+  // the slice re-loads the slice's last row and contributes nothing.
+  constexpr int kBlendRows = 4;
+  const int ls = min(lane, D - 1);  // state of this lane's saved-plane loads
+  for (int bb = b0 + wave; bb < b1; bb += kBlendWaves * kBlendRows) {
+    v4f dv[kBlendRows][2];
+    float cb[kBlendRows], cxk[kBlendRows];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      dv[r] = act[r] ? ld4(dhe + (size_t)b * SH2 + 4 * lane + 256 * r) : v4f{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kBlendRows; ++i) {
+      const int b = min(bb + i * kBlendWaves, b1 - 1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) part += dv[r][q] * wv[r][q];
+      for (int r = 0; r < 2; ++r)
+        dv[i][r] = ld4(dhe + (size_t)b * SH2 + min(4 * lane + 256 * r, SH2 - 4));
+      const float* sv = saved + ((size_t)(b >> 4) * NG + (ls >> 4)) * blk_stride;
+      const int pi = plane_index(b & 15, ls & 15);
+      cb[i] = sv[(size_t)(2 * K - 1) * kPlane + pi];
+      cxk[i] = sv[(size_t)(2 * K) * kPlane + pi];
     }
-    const float dsum = wave_sum(part) * (1.f / (float)D);
-    if (lane < D) dctx[(size_t)b * D + lane] = dsum;
-    float cx = 0.f;
-    if (lane < D) {
-      const float* sv = saved + ((size_t)(b >> 4) * NG + (lane >> 4)) * blk_stride;
-      const int pi = plane_index(b & 15, lane & 15);
-      cx = sv[(size_t)(2 * K - 1) * kPlane + pi] * sv[(size_t)(2 * K) * kPlane + pi];
-    }
-    const float csum = wave_sum(cx);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) acc[r] += dv[r] * csum;
+    for (int i = 0; i < kBlendRows; ++i) {
+      const int b = bb + i * kBlendWaves;
+      const bool live = b < b1;
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part += act[r] ? dv[i][r][q] * wv[r][q] : 0.f;
+      const float dsum = wave_sum(part) * (1.f / (float)D);
+      if (live && lane < D) dctx[(size_t)b * D + lane] = dsum;
+      const float csum = wave_sum(lane < D ? cb[i] * cxk[i] : 0.f);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) acc[r] += live && act[r] ? dv[i][r] * csum : v4f{0.f, 0.f, 0.f, 0.f};
+    }
   }
 #pragma unroll
   for (int r = 0; r < 2; ++r)
