@@ -68,6 +68,7 @@ constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
 __host__ __device__ constexpr int fwd_blocks(int nkc) { return nkc >= 20 ? 2 : 1; }
 __host__ __device__ constexpr int fwd_threads(int nkc) { return fwd_blocks(nkc) * kFwdWaves * 64; }
 constexpr int kFwdPrefetch = 4;    // fp32 history loads each forward wave keeps in flight
+constexpr int kFwdPairPrefetch = 4;  // bf16 history loads (64 features of 8 rows) each wave keeps in flight
 constexpr int kRegRounds = 8;      // rounds whose gate product the forward keeps in registers
 constexpr int kFwdChunkTarget = 512;  // forward work-groups a chunked history aims for
 constexpr int kBwdWaves = 12;
@@ -212,10 +213,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // 32p + 8kg .. +7 of pair p, the first four for chunk 2p, the rest for
   // chunk 2p+1 (the weight slab is staged in the same order).
   constexpr bool PAIR = sizeof(T) == 2;
-#ifndef FWD_PAIR_PF
-#define FWD_PAIR_PF 4
-#endif
-  constexpr int PFP = PAIR ? (FWD_PAIR_PF < NKC / 2 ? FWD_PAIR_PF : NKC / 2) : 0;  // pairs in flight
+  constexpr int PFP = PAIR ? (kFwdPairPrefetch < NKC / 2 ? kFwdPairPrefetch : NKC / 2) : 0;  // loads in flight
   static_assert(!PAIR || PFP % 2 == 0, "bf16 loads go in spans of two pairs");
   // fp32 history on the bf16 matrix cores (SPL): each history value x is
   // split exactly into three bf16 terms as the weights w are (each term at
