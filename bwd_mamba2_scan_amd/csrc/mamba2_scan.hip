@@ -162,9 +162,6 @@ constexpr int kNonTemporal = 0x2;
 __device__ __forceinline__ void st4_nt(__amdgpu_buffer_rsrc_t rs, unsigned off, v4f v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rs, off, 0, kNonTemporal);
 }
-__device__ __forceinline__ void st4_stream(float* p, v4f v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
-}
 
 // Index of (sample smp in 0..15, state n in 0..15) inside a saved plane.  The
 // backward lane (quad kg, state n) reads samples 4kg..4kg+3 as one float4.
