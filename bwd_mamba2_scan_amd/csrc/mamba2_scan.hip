@@ -1394,6 +1394,10 @@ constexpr int kDinWaves = 4;
 constexpr int kDinTargetWGs = 4096 / kDinWaves;      // 16 resident waves per CU
 constexpr int kDinRow = kColBlock + 4;               // padded LDS row of the output transpose
 constexpr int kDinPlaneLds = kPlane + 16;            // padded LDS copy of a saved plane
+// A saved plane in LDS: its four sample quads 68 floats apart instead of 64,
+// so that the B-operand reads (lane (kg, n): sample n, states 4kg + c) of one
+// q-step touch 64 different banks.
+__device__ __forceinline__ int din_pad(int e) { return e + (e >> 6) * 4; }
 constexpr long long kDinMaxRowFloats = 1LL << 26;    // K * SH2 limit: 16 rows of samples stay below 4 GiB
 
 // LDS floats of one wave's tile: the unit's planes (alpha', beta', S_r,
@@ -1530,9 +1534,9 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
   float* tD = tile + 3 * NGT * kDinPlaneLds;
 #pragma unroll
   for (int g = 0; g < NGT; ++g) {
-    *reinterpret_cast<v4f*>(&tA[g * kDinPlaneLds + 4 * lane]) = U.pa[g];
-    *reinterpret_cast<v4f*>(&tB[g * kDinPlaneLds + 4 * lane]) = U.pb[g];
-    if (ROUNDS) *reinterpret_cast<v4f*>(&tS[g * kDinPlaneLds + 4 * lane]) = U.ps[g];
+    *reinterpret_cast<v4f*>(&tA[g * kDinPlaneLds + din_pad(4 * lane)]) = U.pa[g];
+    *reinterpret_cast<v4f*>(&tB[g * kDinPlaneLds + din_pad(4 * lane)]) = U.pb[g];
+    if (ROUNDS) *reinterpret_cast<v4f*>(&tS[g * kDinPlaneLds + din_pad(4 * lane)]) = U.ps[g];
     *reinterpret_cast<v4f*>(&tD[(g * 64 + lane) * 4]) = U.pd[g];
   }
   __builtin_amdgcn_wave_barrier();
@@ -1551,7 +1555,7 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
       for (int e = 0; e < 8; ++e) {
         const int kap = 32 * h + 8 * kg + e;
         const int st = kap < D ? kap : kap - D;  // state
-        const int pidx = (st >> 4) * kDinPlaneLds + plane_index(n, st & 15);
+        const int pidx = (st >> 4) * kDinPlaneLds + din_pad(plane_index(n, st & 15));
         float dc = tD[n * D + st];
         if (ROUNDS && !readout) dc *= tS[pidx];
         const float x = (readout || kap < D) ? tA[pidx] : tB[pidx];
@@ -1577,7 +1581,7 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     const int sn = 4 * kg + (i & 3);
-    const int pidx = (i >> 2) * kDinPlaneLds + plane_index(n, sn);
+    const int pidx = (i >> 2) * kDinPlaneLds + din_pad(plane_index(n, sn));
     float dc = tD[n * D + 16 * (i >> 2) + sn];
     if (ROUNDS && !readout) dc *= tS[pidx];
     da[i] = dc * tA[pidx];
