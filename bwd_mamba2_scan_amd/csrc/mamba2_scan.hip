@@ -1400,10 +1400,13 @@ constexpr int kDinPlaneLds = kPlane + 16;            // padded LDS copy of a sav
 __device__ __forceinline__ int din_pad(int e) { return e + (e >> 6) * 4; }
 constexpr long long kDinMaxRowFloats = 1LL << 26;    // K * SH2 limit: 16 rows of samples stay below 4 GiB
 
-// LDS floats of one wave's tile: the unit's planes (alpha', beta', S_r,
-// d_context; NGT of each), reused afterwards for the output transpose.
+// LDS floats of one wave's tile: the unit's planes (alpha', beta', S_r; NGT
+// of each) and the block's d_context rows (padded by 4 floats), reused
+// afterwards for the output transpose.
 __host__ __device__ constexpr int din_tile_floats(int ngt) {
-  return 4 * ngt * kDinPlaneLds > kBlock * kDinRow ? 4 * ngt * kDinPlaneLds : kBlock * kDinRow;
+  return 3 * ngt * kDinPlaneLds + kBlock * (ngt * kGroup + 4) > kBlock * kDinRow
+             ? 3 * ngt * kDinPlaneLds + kBlock * (ngt * kGroup + 4)
+             : kBlock * kDinRow;
 }
 
 template <int NGT>
@@ -1537,7 +1540,12 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
     *reinterpret_cast<v4f*>(&tA[g * kDinPlaneLds + din_pad(4 * lane)]) = U.pa[g];
     *reinterpret_cast<v4f*>(&tB[g * kDinPlaneLds + din_pad(4 * lane)]) = U.pb[g];
     if (ROUNDS) *reinterpret_cast<v4f*>(&tS[g * kDinPlaneLds + din_pad(4 * lane)]) = U.ps[g];
-    *reinterpret_cast<v4f*>(&tD[(g * 64 + lane) * 4]) = U.pd[g];
+    {
+      // d_context rows 4 floats apart beyond their D (fewer bank conflicts
+      // in the column reads below)
+      const int e = (g * 64 + lane) * 4;
+      *reinterpret_cast<v4f*>(&tD[(e / D) * (D + 4) + e % D]) = U.pd[g];
+    }
   }
   __builtin_amdgcn_wave_barrier();
   v4f acc[4];
@@ -1556,7 +1564,7 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
         const int kap = 32 * h + 8 * kg + e;
         const int st = kap < D ? kap : kap - D;  // state
         const int pidx = (st >> 4) * kDinPlaneLds + din_pad(plane_index(n, st & 15));
-        float dc = tD[n * D + st];
+        float dc = tD[n * (D + 4) + st];
         if (ROUNDS && !readout) dc *= tS[pidx];
         const float x = (readout || kap < D) ? tA[pidx] : tB[pidx];
         v[e] = (readout && kap >= D) ? 0.f : dc * x;
@@ -1582,7 +1590,7 @@ __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const 
   for (int i = 0; i < NQ; ++i) {
     const int sn = 4 * kg + (i & 3);
     const int pidx = (i >> 2) * kDinPlaneLds + din_pad(plane_index(n, sn));
-    float dc = tD[n * D + 16 * (i >> 2) + sn];
+    float dc = tD[n * (D + 4) + 16 * (i >> 2) + sn];
     if (ROUNDS && !readout) dc *= tS[pidx];
     da[i] = dc * tA[pidx];
     db[i] = dc * tB[pidx];
