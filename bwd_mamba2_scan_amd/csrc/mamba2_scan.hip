@@ -242,11 +242,11 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   __shared__ v4u sWab[WSPLIT ? 6 * NP * 64 : 1];  // [mat A|B][term hi|mid|lo][pair][lane]: 8 bf16
   __shared__ v4f sWc[CT ? 1 : NKC * 64];
   __shared__ v4f sT[CT ? kFwdBlocks * kFwdWaves * 128 : 1];  // CT: [wave][half j][64 slots]
-  __shared__ float sXa[kFwdBlocks][kChunk][kPlane];
-  __shared__ float sXb[kFwdBlocks][kChunk][kPlane];
+  __shared__ __attribute__((aligned(16))) float sXa[kFwdBlocks][kChunk][kPlane];
+  __shared__ __attribute__((aligned(16))) float sXb[kFwdBlocks][kChunk][kPlane];
   // readout partials; with BFM they share sXa's memory (summed into c
   // before the first exchange writes it), which keeps two work-groups per CU
-  __shared__ float sCbuf[WSPLIT ? 1 : kFwdBlocks * kFwdWaves * kPlane];
+  __shared__ __attribute__((aligned(16))) float sCbuf[WSPLIT ? 4 : kFwdBlocks * kFwdWaves * kPlane];
   float(*sC)[kFwdWaves][kPlane] = WSPLIT ? sXa : reinterpret_cast<float(*)[kFwdWaves][kPlane]>(sCbuf);
 
   const int D = NG * kGroup;
@@ -498,8 +498,8 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
         for (int i = 0; i < 4; ++i) acc = mfma16x16x4(ok ? hc[r][i] : 0.f, bv[i], acc);
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sC[half][wave][(4 * kg + r) * kGroup + m] = acc[r];
+    // result rows 4kg..4kg+3 at state m: one float4 in the plane layout
+    *reinterpret_cast<v4f*>(&sC[half][wave][kg * 64 + 4 * m]) = acc;
   }
   if constexpr (WSPLIT) {
     // sum the readout now: the partials' memory is sXa's
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     if (scanner) {
       float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < kFwdWaves; ++w) s += sC[half][w][smp * kGroup + m];
+      for (int w = 0; w < kFwdWaves; ++w) s += sC[half][w][plane_index(smp, m)];
       c = s;
     }
     __syncthreads();
@@ -631,20 +631,24 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       // stability multiplier m scales the gate and its derivative (m = 1
       // leaves every product bit-identical).  The exchange carries m*g and b;
       // m g (1 - g) stays here for this step's alpha' below.
+      v4f mg;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = acca[r];
         const float e = __expf(-a);
         const float g = __builtin_amdgcn_rcpf(1.f + e);
         gq[r] = g * (a > 0.f ? e * g : 1.f - g) * mstab;
-        sXa[half][wave][(4 * kg + r) * kGroup + m] = g * mstab;
-        sXb[half][wave][(4 * kg + r) * kGroup + m] = accb[r];
+        mg[r] = g * mstab;
       }
+      // the exchange holds tiles in the plane layout: this lane's four
+      // samples 4kg..4kg+3 at state m are one float4
+      *reinterpret_cast<v4f*>(&sXa[half][wave][kg * 64 + 4 * m]) = mg;
+      *reinterpret_cast<v4f*>(&sXb[half][wave][kg * 64 + 4 * m]) = accb;
     }
     __syncthreads();
 
     if (scanner) {
-      const int idx = smp * kGroup + m;
+      const int idx = plane_index(smp, m);
       if (!WSPLIT && ch == r0) {
         float s = 0.f;
 #pragma unroll
@@ -702,12 +706,12 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(sv + (size_t)(2 * ts) * kPlane, st_ok ? 2 * kPlane * sizeof(float) : 0u);
       v4f al, be;
+      const v4f xq = *reinterpret_cast<const v4f*>(&sXa[half][wave][kg * 64 + 4 * m]);
+      const v4f pq = *reinterpret_cast<const v4f*>(&sXb[half][wave][kg * 64 + 4 * m]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float xv = sXa[half][wave][(4 * kg + r) * kGroup + m];
-        const float Pv = sXb[half][wave][(4 * kg + r) * kGroup + m];
-        al[r] = Pv * (xv * gq[r]);
-        be[r] = Pv;
+        al[r] = pq[r] * (xq[r] * gq[r]);
+        be[r] = pq[r];
       }
       const unsigned off = (unsigned)(toff * sizeof(float));
       st4_nt(rs, off, mode == 1 ? sa : al);
@@ -721,11 +725,11 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // rather than kept in registers through the rounds.
   if constexpr (!PAIR) {
     if (he != nullptr && NG == 1 && cidx == C - 1) {  // uniform over the work-group
-      if (scanner) sC[half][0][smp * kGroup + m] = c * x;
+      if (scanner) sC[half][0][plane_index(smp, m)] = c * x;
       __syncthreads();
       float sum = 0.f;
 #pragma unroll
-      for (int s2 = 0; s2 < kGroup; ++s2) sum += sC[half][0][m * kGroup + s2];  // states in order
+      for (int s2 = 0; s2 < kGroup; ++s2) sum += sC[half][0][plane_index(m, s2)];  // states in order
       const float scale = sum * (1.f / (float)kGroup);                         // exact: D = 16
       const int b_row = blk * kBlock + m;
 #pragma unroll
