@@ -1154,17 +1154,17 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   }
 
   // Result lane (g = kg, n = m), element r of tile q: feature row
-  // jl = 16*g + 4*r + q of the column block, state n.
+  // jl = 16*g + 4*r + q of the column block, state n.  Slices keep that
+  // register order, [plane][g][q][n][r], so each lane writes whole float4s
+  // (the reduce maps the order back onto dW).
 #pragma unroll
   for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sRed[wave][pl * (kColBlock * kGroup) + (16 * kg + 4 * r + q) * kGroup + m] = acc[q][pl][r];
+      *reinterpret_cast<v4f*>(&sRed[wave][pl * (kColBlock * kGroup) + (kg * 4 + q) * 64 + m * 4]) = acc[q][pl];
   __syncthreads();
 
-  // Slice layout: ws[sg][p][jb][plane][jl][n].  Written through to memory
+  // Slice layout: ws[sg][p][jb][plane][g][q][n][r].  Written through to memory
   // (16-byte stores with system-scope coherence) so that no dirty L2 lines
   // remain to be written back before the reduce can start.
   float* out = ws + ((size_t)sg * P + p) * ((size_t)SH2 * 3 * kGroup) + (size_t)jb * (3 * kColBlock * kGroup);
@@ -1243,17 +1243,16 @@ __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
   const v4f tot = reduce_slices(ws + (size_t)sg * P * per_sg + o, (size_t)per_sg, P, ok, grp, ql, sPart);
   if (grp != 0 || !ok) return;
 
+  // slice order [jb][plane][g][q][n][r]: element r of this quad is feature
+  // row jl = 16g + 4r + q of column block jb, state n
   const int jb = o / (3 * kColBlock * kGroup);
   const int rem = o - jb * (3 * kColBlock * kGroup);
   const int pl = rem / (kColBlock * kGroup);
   const int rem2 = rem - pl * (kColBlock * kGroup);
-  const int jl = rem2 / kGroup;
-  const int n = rem2 - jl * kGroup;  // multiple of 4
-  float* dst = (pl == 0 ? dWA : (pl == 1 ? dWB : dWC)) + (size_t)(jb * kColBlock + jl) * D + sg * kGroup + n;
-  dst[0] = tot[0];
-  dst[1] = tot[1];
-  dst[2] = tot[2];
-  dst[3] = tot[3];
+  const int g = rem2 >> 8, q = (rem2 >> 6) & 3, n = (rem2 >> 2) & 15;
+  float* dst = (pl == 0 ? dWA : (pl == 1 ? dWB : dWC)) + (size_t)(jb * kColBlock + 16 * g + q) * D + sg * kGroup + n;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[(size_t)(4 * r) * D] = tot[r];
 }
 
 // ---------------------------------------------------------------------------
