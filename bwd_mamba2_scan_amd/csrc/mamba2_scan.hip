@@ -1395,6 +1395,7 @@ __global__ __launch_bounds__(kBlendWaves * 64) void blend_bwd_kernel(
 // stay exact and the next unit's requests stay in flight.
 constexpr int kDinWaves = 4;
 constexpr int kDinTargetWGs = 4096 / kDinWaves;      // 16 resident waves per CU
+constexpr int kDinTargetWGsRounds = 2 * kDinTargetWGs;  // multi-round histories: shorter slices balance better
 constexpr int kDinRow = kColBlock + 4;               // padded LDS row of the output transpose
 constexpr int kDinPlaneLds = kPlane + 16;            // padded LDS copy of a saved plane
 // A saved plane in LDS: its four sample quads 68 floats apart instead of 64,
@@ -1946,13 +1947,15 @@ size_t blend_ws_bytes(const Plan& pl) {
   return blend_ws_offset(pl) + (size_t)kBlendSlices * pl.SH2 * sizeof(float);
 }
 
-// Chunk size: about kDinTargetWGs work-groups over all chunks and column blocks.
 // Units per work-group: the (block, t) units of all blocks, in order, split
-// into slices so that about kDinTargetWGs work-groups run (at least one unit
-// per wave), whatever the mix of samples and history length.
+// into slices so that about kDinTargetWGs work-groups run (twice as many when
+// K spans several rounds: K = 64 and long_few ran 3 % faster, the pages'
+// shape 5 % slower), at least one unit per wave, whatever the mix of samples
+// and history length.
 int dinput_upw(const Plan& pl) {
   const long long units = (long long)pl.NB * (pl.K + 1);
-  const long long slices = (kDinTargetWGs + pl.NJB - 1) / pl.NJB;
+  const int target = pl.K > kChunk ? kDinTargetWGsRounds : kDinTargetWGs;
+  const long long slices = (target + pl.NJB - 1) / pl.NJB;
   long long upw = (units + slices - 1) / slices;
   if (upw < kDinWaves) upw = kDinWaves;
   return (int)(upw > units ? units : upw);
