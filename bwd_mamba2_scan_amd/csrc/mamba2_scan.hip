@@ -315,10 +315,8 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
     // W_A, W_B: a task is (matrix, octet o of rows 8o..8o+7, states
     // 4*s4..4*s4+3); per state n it writes the eight rows' three terms as
     // three 16-byte entries (pair o/4, lane (o%4, n)).
-    constexpr int NTASK = 2 * (SH2 / 8) * 4;  // = SH2 <= half the threads
-    static_assert(2 * NTASK <= kFwdThreads, "one task per thread");
-    if (tid < NTASK) {
-      const int task = tid;
+    constexpr int NTASK = 2 * (SH2 / 8) * 4;  // = SH2
+    for (int task = tid; task < NTASK; task += kFwdThreads) {
       const int mat = task / ((SH2 / 8) * 4);
       const int o = (task >> 2) % (SH2 / 8);
       const int s4 = task & 3;
