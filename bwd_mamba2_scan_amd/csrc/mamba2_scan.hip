@@ -68,6 +68,7 @@ constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
 __host__ __device__ constexpr int fwd_blocks(int nkc) { return nkc >= 20 ? 2 : 1; }
 __host__ __device__ constexpr int fwd_threads(int nkc) { return fwd_blocks(nkc) * kFwdWaves * 64; }
 constexpr int kFwdPrefetch = 4;    // fp32 history loads each forward wave keeps in flight
+constexpr int kCUs = 256;            // compute units of an MI355X
 constexpr int kFwdPairPrefetch = 4;  // bf16 history loads (64 features of 8 rows) each wave keeps in flight
 constexpr int kRegRounds = 8;      // rounds whose gate product the forward keeps in registers
 constexpr int kFwdChunkTarget = 512;  // forward work-groups a chunked history aims for
@@ -194,23 +195,29 @@ __host__ __device__ __forceinline__ int saved_planes(int K) {
 // REPLAY (the second pass of a chunked history): the step projections a, b
 // come from the alpha'/beta' slots, where the summary pass left them, instead
 // of from h_history; only W_C is staged, for the readout.
-template <int NKC, class T, bool REPLAY = false>  // SH2 / 16 trunk chunks; T = fp32 or bf16 trunk inputs
-__global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
+// NBLK sample blocks per work-group: two for SH2 >= 320 (one work-group per
+// CU, 16 waves), one when two-block work-groups would leave CUs idle (then
+// 8 waves, with room for twice the loads in flight).
+template <int NKC, class T, bool REPLAY = false, int NBLK = fwd_blocks(NKC)>  // SH2 / 16 trunk chunks;
+// T = fp32 or bf16 trunk inputs
+__global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
     int B, int K, int NG, int NB,
     const T* __restrict__ H, const T* __restrict__ hs2,
     const float* __restrict__ WA, const float* __restrict__ WB, const float* __restrict__ WC,
     const float* __restrict__ stab, float* __restrict__ ctx, float* __restrict__ saved,
     int L, int C, int mode, const float* __restrict__ tw, float* __restrict__ he) {
   constexpr int SH2 = NKC * 16;
-  constexpr int kFwdBlocks = fwd_blocks(NKC);
-  constexpr int kFwdThreads = fwd_threads(NKC);
+  constexpr int kFwdBlocks = NBLK;
+  constexpr int kFwdThreads = NBLK * kFwdWaves * 64;
+  constexpr bool kDeepSingle = NBLK == 1 && fwd_blocks(NKC) == 2;  // lone block of a wide trunk
   constexpr int NCR = (NKC + kFwdWaves - 1) / kFwdWaves;                   // readout chunks per wave
   constexpr int NCRP = (NKC / 2 + kFwdWaves - 1) / kFwdWaves;              // readout pairs per wave (bf16)
   // bf16 inputs come in pairs of chunks: lane (kg, m) holds features
   // 32p + 8kg .. +7 of pair p, the first four for chunk 2p, the rest for
   // chunk 2p+1 (the weight slab is staged in the same order).
   constexpr bool PAIR = sizeof(T) == 2;
-  constexpr int PFP = PAIR ? (kFwdPairPrefetch < NKC / 2 ? kFwdPairPrefetch : NKC / 2) : 0;  // loads in flight
+  constexpr int PFP = PAIR ? (kDeepSingle ? 4 : (kFwdPairPrefetch < NKC / 2 ? kFwdPairPrefetch : NKC / 2))
+                           : 0;  // loads in flight
   static_assert(!PAIR || PFP % 2 == 0, "bf16 loads go in spans of two pairs");
   // fp32 history on the bf16 matrix cores (SPL): each history value x is
   // split exactly into three bf16 terms as the weights w are (each term at
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(fwd_threads(NKC)) void fwd_kernel(
   // 37 % of their matrix-core cycles at the two peaks; the split's
   // registers leave room for four loads in flight per wave.
   constexpr bool SPL = !PAIR && !REPLAY;
-  constexpr int PF = PAIR ? 2 * PFP : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC);  // chunks in flight
+  constexpr int PF = PAIR ? 2 * PFP : (kDeepSingle ? 8 : (kFwdPrefetch < NKC ? kFwdPrefetch : NKC));  // in flight
   static_assert(PAIR || PF % 2 == 0, "fp32 loads go in pairs");
   // bf16 trunk inputs feed bf16 MFMAs directly: each weight is split
   // exactly into three bf16 terms (hi + mid + lo == W for every fp32 W above
@@ -1843,13 +1850,23 @@ void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const
   constexpr int kFwdThreads = fwd_threads(NKC);
   const int pairs = (pl.NB + kFwdBlocks - 1) / kFwdBlocks;
   const int grid = 8 * pl.NG * ((pairs * C + 7) / 8);
-  if (C == 1) {
+  // Two-block work-groups that would leave CUs idle: one block each instead
+  // (4096 samples at SH2 = 320/512: forward 18 -> 14 / 23 -> 19 us; with
+  // every CU busy the two-block form is faster: 8192 samples 34 vs 38 us).
+  if (kFwdBlocks == 2 && (long long)pairs * pl.NG * C < kCUs) {
+    const int grid1 = 8 * pl.NG * ((pl.NB * C + 7) / 8);
+    hipLaunchKernelGGL((fwd_kernel<NKC, T, false, 1>), dim3(grid1), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG,
+                       pl.NB, H, hs2, WA, WB, WC, stab, ctx, saved, L, C, C == 1 ? 0 : 1, C == 1 ? tw : nullptr,
+                       C == 1 ? he : nullptr);
+    if (C == 1) return;
+  } else if (C == 1) {
     hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
                        H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 0, tw, he);
     return;
+  } else {
+    hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
+                       hs2, WA, WB, WC, stab, ctx, saved, L, C, 1, nullptr, nullptr);
   }
-  hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
-                     hs2, WA, WB, WC, stab, ctx, saved, L, C, 1, nullptr, nullptr);
   const int nseg = carry_segments(C);  // C <= kFwdChunkTarget, so nseg <= kFwdChunkTarget / kCarrySeg
   hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG * nseg), dim3(kCarryThreads), 0, st, pl.NB * pl.NG, pl.K,
                      L, C, nseg, saved);

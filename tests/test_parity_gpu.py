@@ -273,6 +273,7 @@ LONG_FEW_SHAPES = [
     (3, 300, 64, 64),
     (17, 160, 192, 16),
     (5, 8192, 64, 16),    # one sample block: 512 history chunks, the carry's 32 segments
+    (20, 96, 384, 16),    # a wide trunk in chunks: one-block summary pass, two-block replay
 ]
 
 
