@@ -311,26 +311,36 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
   }
   const float mstab = stab != nullptr ? stab[0] : 1.f;
 
-  // (1) Weight slab, staged before any history load is issued: the slab's
+  // (1) Weight slab, loaded before any history load is issued: the slab's
   // loads would otherwise queue behind the CU's history stream and hold every
   // MFMA back.  W_A and W_B go in as three bf16 terms each, in the
   // v_mfma_f32_16x16x32_bf16 B-operand layout; the replay pass stages only
   // W_C, in fp32 for the readout, where entry (kc, l) holds
   // W[kc*16 + 4*(l>>4) + i][sg*16 + (l&15)] for i = 0..3 (pair order for
   // bf16 inputs).
+  // W_A, W_B (split terms): a task is (matrix, octet o of rows 8o..8o+7,
+  // states 4*s4..4*s4+3), one per thread; per state n it writes the eight
+  // rows' three terms as three 16-byte entries (pair o/4, lane (o%4, n)).
+  // The rows are loaded here and waited for; the split and its LDS writes
+  // run after the first history loads have gone out, under their latency.
+  constexpr int NTASK = 2 * (SH2 / 8) * 4;  // = SH2
+  static_assert(!WSPLIT || NTASK <= kFwdThreads, "one weight task per thread");
+  const int w_mat = tid / ((SH2 / 8) * 4);
+  const int w_o = (tid >> 2) % (SH2 / 8);
+  const int w_s4 = tid & 3;
+  v4f wst[WSPLIT ? 8 : 1];
   if constexpr (WSPLIT) {
-    // W_A, W_B: a task is (matrix, octet o of rows 8o..8o+7, states
-    // 4*s4..4*s4+3); per state n it writes the eight rows' three terms as
-    // three 16-byte entries (pair o/4, lane (o%4, n)).
-    constexpr int NTASK = 2 * (SH2 / 8) * 4;  // = SH2
-    for (int task = tid; task < NTASK; task += kFwdThreads) {
-      const int mat = task / ((SH2 / 8) * 4);
-      const int o = (task >> 2) % (SH2 / 8);
-      const int s4 = task & 3;
-      const float* W = mat == 0 ? WA : WB;
-      v4f w[8];
+    if (tid < NTASK) {
+      const float* W = w_mat == 0 ? WA : WB;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) w[jj] = ld4(W + (size_t)(8 * o + jj) * D + sg * kGroup + 4 * s4);
+      for (int jj = 0; jj < 8; ++jj) wst[jj] = ld4(W + (size_t)(8 * w_o + jj) * D + sg * kGroup + 4 * w_s4);
+      __asm__ volatile("" ::"v"(wst[7][0]));  // wait for the rows (they return in order)
+    }
+  }
+  auto stage_split = [&]() {
+    if (tid < NTASK) {
+      const int mat = w_mat, o = w_o, s4 = w_s4;
+      const v4f* w = wst;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v8bf th, tm, tl;
@@ -351,7 +361,8 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
         sWab[(mat * 3 + 2) * NP * 64 + e] = __builtin_bit_cast(v4u, tl);
       }
     }
-  } else {
+  };
+  if constexpr (!WSPLIT) {
     // REPLAY: only W_C, for the readout
     constexpr int NW4 = SH2 * 4;  // float4s of the slab
     constexpr int NWT = (NW4 + kFwdThreads - 1) / kFwdThreads;
@@ -467,6 +478,7 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
   // otherwise sink them to their first use)
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (WSPLIT) stage_split();  // read after the barrier below
 
   // (3) readout partial over this wave's chunks (a clamped chunk past the
   // last one enters as zeros: no branch, so no load is moved under one)
