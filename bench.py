@@ -186,8 +186,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scan's batch shards with no communication in the "
-              "forward and one small all-reduce of dW in the backward, and this build runs on a "
-              "single MI355X. Run with --gpus 1.", file=sys.stderr)
+              "forward and one small all-reduce of dW in the backward; the multi-GPU path is not "
+              "built. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
