@@ -1,6 +1,6 @@
 """Parity of the HIP path against the CPU oracle, on an MI355X.
 
-Tolerances (benchmark spec, restated):
+Tolerances (the accuracy the path is held to):
   * outputs (context, and d_a, d_b, d_c when requested): elementwise
     |gpu - ref| <= 1e-4 * (1 + |ref|)
   * weight gradients: sum|gpu - ref| / sum|ref| <= 1e-3 per matrix.
