@@ -274,6 +274,8 @@ LONG_FEW_SHAPES = [
     (17, 160, 192, 16),
     (5, 8192, 64, 16),    # one sample block: 512 history chunks, the carry's 32 segments
     (20, 96, 384, 16),    # a wide trunk in chunks: one-block summary pass, two-block replay
+    (32, 2024, 256, 16),  # 63 chunks of 32 steps, the remainder merged into a 40-step last chunk
+    (32, 2040, 256, 16),  # 64 chunks, the last one 24 steps
 ]
 
 
