@@ -59,7 +59,18 @@ _SIGNATURES = {
     "mamba2_scan_bwd_bf16": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 8 + [_c_size, _c_vp]),
     "mamba2_scan_bwd_partials_bf16": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 5 + [_c_size, _c_vp]),
     "mamba2_scan_strerror": (ctypes.c_char_p, [_c_int]),
+    "mamba2_scan_fwd_plan": (_c_int, [_c_int] * 4 + [_c_vp, _c_int]),
 }
+
+
+class Launch(ctypes.Structure):
+    """mamba2_scan_launch: one kernel launch of a forward call."""
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("kernel", "sample_blocks", "pass_", "chunks", "chunk_steps", "grid", "threads")]
+
+
+KERNEL_NAMES = {0: "fwd", 1: "carry"}
+PASS_NAMES = {0: "full", 1: "summary", 2: "carry", 3: "replay"}
 
 
 def lib():
@@ -97,6 +108,16 @@ def saved_bytes(B: int, K: int, SH2: int, D: int) -> int:
 
 def workspace_bytes(B: int, K: int, SH2: int, D: int) -> int:
     return int(lib().mamba2_scan_bwd_workspace_bytes(B, K, SH2, D))
+
+
+def fwd_plan(B: int, K: int, SH2: int, D: int) -> list[dict]:
+    """The kernel launches a forward call enqueues for these dimensions (host only, no GPU)."""
+    buf = (Launch * 4)()
+    n = lib().mamba2_scan_fwd_plan(B, K, SH2, D, ctypes.cast(buf, ctypes.c_void_p), 4)
+    _raise(n if n < 0 else OK, "mamba2_scan_fwd_plan")
+    return [{"kernel": KERNEL_NAMES[l.kernel], "sample_blocks": l.sample_blocks, "pass": PASS_NAMES[l.pass_],
+             "chunks": l.chunks, "chunk_steps": l.chunk_steps, "grid": l.grid, "threads": l.threads}
+            for l in buf[:n]]
 
 
 # ----------------------------------------------------------------- torch side

@@ -719,7 +719,9 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
     // past the chunk's last step (and in the summary pass), so no memory
     // operation sits under a branch while the next round's loads are in
     // flight.  (Every wave reads back only its own slots here, and writes
-    // them again only after its next projection, so no barrier is needed.)
+    // them again only after its next projection, so no barrier is needed
+    // within the rounds; whatever writes these slots after the last round
+    // -- the fused blend below -- waits at a barrier first.)
     {
       const bool st_ok = t < t1 && blk_ok;
       const int ts = min(t, t1 - 1);
@@ -745,6 +747,11 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
   // rather than kept in registers through the rounds.
   if constexpr (!PAIR) {
     if (he != nullptr && NG == 1 && cidx == C - 1) {  // uniform over the work-group
+      // sC[half][0] is wave 0's exchange slot when the weights are split
+      // (sC aliases sXa): wave 0 may still be reading it for its last
+      // alpha' store above, so every wave passes this barrier before the
+      // scanners overwrite it.
+      __syncthreads();
       if (scanner) sC[half][0][plane_index(smp, m)] = c * x;
       __syncthreads();
       float sum = 0.f;
@@ -1855,38 +1862,74 @@ void fwd_chunks(const Plan& pl, int* L, int* C) {
   *C = cc;
 }
 
+// The forward's launches for a shape, in order: what launch_fwd enqueues and
+// mamba2_scan_fwd_plan reports.  Returns the count (1 or 3).
+//  * C == 1: one full pass (projections, scan, saved terms, context).
+//  * C > 1 (chunked history): a summary pass, the carry across chunks, then
+//    the replay pass.
+// Work-groups hold one or two sample blocks: two from SH2 = 320 on
+// (fwd_blocks), except where two-block work-groups would leave CUs idle,
+// when a full or summary pass takes one block each (4096 samples at
+// SH2 = 320/512: forward 18 -> 14 / 23 -> 19 us; with every CU busy the
+// two-block form is faster: 8192 samples 34 vs 38 us).  The replay pass
+// always takes fwd_blocks(SH2/16) blocks.
+int fwd_plan(const Plan& pl, mamba2_scan_launch* out) {
+  int L, C;
+  fwd_chunks(pl, &L, &C);
+  const int nkc = pl.SH2 / 16;
+  const int nblk = fwd_blocks(nkc);
+  const int pairs = (pl.NB + nblk - 1) / nblk;
+  const bool lone = nblk == 2 && (long long)pairs * pl.NG * C < kCUs;
+  const int first_blk = lone ? 1 : nblk;
+  const int first_units = lone ? pl.NB : pairs;
+  auto set = [&](mamba2_scan_launch& l, int kernel, int blocks, int pass, int grid, int threads) {
+    l.kernel = kernel;
+    l.sample_blocks = blocks;
+    l.pass = pass;
+    l.chunks = C;
+    l.chunk_steps = L;
+    l.grid = grid;
+    l.threads = threads;
+  };
+  set(out[0], MAMBA2_SCAN_KERNEL_FWD, first_blk, C == 1 ? MAMBA2_SCAN_PASS_FULL : MAMBA2_SCAN_PASS_SUMMARY,
+      8 * pl.NG * ((first_units * C + 7) / 8), first_blk * kFwdWaves * 64);
+  if (C == 1) return 1;
+  const int nseg = carry_segments(C);  // C <= kFwdChunkTarget, so nseg <= kFwdChunkTarget / kCarrySeg
+  set(out[1], MAMBA2_SCAN_KERNEL_CARRY, 0, MAMBA2_SCAN_PASS_CARRY, pl.NB * pl.NG * nseg, kCarryThreads);
+  set(out[2], MAMBA2_SCAN_KERNEL_FWD, nblk, MAMBA2_SCAN_PASS_REPLAY, 8 * pl.NG * ((pairs * C + 7) / 8),
+      nblk * kFwdWaves * 64);
+  return 3;
+}
+
 template <int NKC, class T>
 void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const float* WB,
                 const float* WC, const float* stab, float* ctx, float* saved, hipStream_t st,
                 const float* tw, float* he) {
-  int L, C;
-  fwd_chunks(pl, &L, &C);
-  constexpr int kFwdBlocks = fwd_blocks(NKC);
-  constexpr int kFwdThreads = fwd_threads(NKC);
-  const int pairs = (pl.NB + kFwdBlocks - 1) / kFwdBlocks;
-  const int grid = 8 * pl.NG * ((pairs * C + 7) / 8);
-  // Two-block work-groups that would leave CUs idle: one block each instead
-  // (4096 samples at SH2 = 320/512: forward 18 -> 14 / 23 -> 19 us; with
-  // every CU busy the two-block form is faster: 8192 samples 34 vs 38 us).
-  if (kFwdBlocks == 2 && (long long)pairs * pl.NG * C < kCUs) {
-    const int grid1 = 8 * pl.NG * ((pl.NB * C + 7) / 8);
-    hipLaunchKernelGGL((fwd_kernel<NKC, T, false, 1>), dim3(grid1), dim3(kFwdWaves * 64), 0, st, pl.B, pl.K, pl.NG,
-                       pl.NB, H, hs2, WA, WB, WC, stab, ctx, saved, L, C, C == 1 ? 0 : 1, C == 1 ? tw : nullptr,
-                       C == 1 ? he : nullptr);
-    if (C == 1) return;
-  } else if (C == 1) {
-    hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
-                       H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 0, tw, he);
-    return;
-  } else {
-    hipLaunchKernelGGL((fwd_kernel<NKC, T>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB, H,
-                       hs2, WA, WB, WC, stab, ctx, saved, L, C, 1, nullptr, nullptr);
+  mamba2_scan_launch ls[3];
+  const int n = fwd_plan(pl, ls);
+  for (int i = 0; i < n; ++i) {
+    const mamba2_scan_launch& l = ls[i];
+    const dim3 grid(l.grid), block(l.threads);
+    // the blend rides on the pass that writes context
+    const bool last = l.pass == MAMBA2_SCAN_PASS_FULL || l.pass == MAMBA2_SCAN_PASS_REPLAY;
+    const float* twp = last ? tw : nullptr;
+    float* hep = last ? he : nullptr;
+    if (l.kernel == MAMBA2_SCAN_KERNEL_CARRY) {
+      hipLaunchKernelGGL(fwd_carry_kernel, grid, block, 0, st, pl.NB * pl.NG, pl.K, l.chunk_steps, l.chunks,
+                         l.grid / (pl.NB * pl.NG), saved);
+    } else if (l.pass == MAMBA2_SCAN_PASS_REPLAY) {
+      hipLaunchKernelGGL((fwd_kernel<NKC, T, true>), grid, block, 0, st, pl.B, pl.K, pl.NG, pl.NB, H, hs2, WA, WB,
+                         WC, stab, ctx, saved, l.chunk_steps, l.chunks, 2, twp, hep);
+    } else if (l.sample_blocks == 1) {
+      hipLaunchKernelGGL((fwd_kernel<NKC, T, false, 1>), grid, block, 0, st, pl.B, pl.K, pl.NG, pl.NB, H, hs2, WA,
+                         WB, WC, stab, ctx, saved, l.chunk_steps, l.chunks, l.pass == MAMBA2_SCAN_PASS_FULL ? 0 : 1,
+                         twp, hep);
+    } else if constexpr (fwd_blocks(NKC) == 2) {
+      hipLaunchKernelGGL((fwd_kernel<NKC, T, false, 2>), grid, block, 0, st, pl.B, pl.K, pl.NG, pl.NB, H, hs2, WA,
+                         WB, WC, stab, ctx, saved, l.chunk_steps, l.chunks, l.pass == MAMBA2_SCAN_PASS_FULL ? 0 : 1,
+                         twp, hep);
+    }
   }
-  const int nseg = carry_segments(C);  // C <= kFwdChunkTarget, so nseg <= kFwdChunkTarget / kCarrySeg
-  hipLaunchKernelGGL(fwd_carry_kernel, dim3(pl.NB * pl.NG * nseg), dim3(kCarryThreads), 0, st, pl.NB * pl.NG, pl.K,
-                     L, C, nseg, saved);
-  hipLaunchKernelGGL((fwd_kernel<NKC, T, true>), dim3(grid), dim3(kFwdThreads), 0, st, pl.B, pl.K, pl.NG, pl.NB,
-                     H, hs2, WA, WB, WC, stab, ctx, saved, L, C, 2, tw, he);
 }
 
 int check_bwd_common(const Plan& pl, const void* H, const void* hs2, const void* saved, size_t saved_bytes,
@@ -2201,6 +2244,17 @@ int mamba2_scan_bwd_input(int B, int K, int SH2, int STATE_D, const float* W_A, 
     default: return MAMBA2_SCAN_EUNSUPPORTED;
   }
   return launch_status();
+}
+
+int mamba2_scan_fwd_plan(int B, int K, int SH2, int STATE_D, mamba2_scan_launch* launches, int max_launches) {
+  Plan pl;
+  const int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  if (max_launches > 0 && launches == nullptr) return MAMBA2_SCAN_ENULL;
+  mamba2_scan_launch ls[3];
+  const int n = fwd_plan(pl, ls);
+  for (int i = 0; i < n && i < max_launches; ++i) launches[i] = ls[i];
+  return n;
 }
 
 const char* mamba2_scan_strerror(int status) {

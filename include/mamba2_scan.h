@@ -240,6 +240,42 @@ int mamba2_scan_bwd_bf16(int B, int K, int SH2, int STATE_D,
 /* Static text for a status code. */
 const char* mamba2_scan_strerror(int status);
 
+/*
+ * Launch plan of a forward call (pure host code: touches no device and
+ * enqueues nothing).  It names each kernel launch that mamba2_scan_fwd,
+ * mamba2_scan_fwd_bf16 or mamba2_scan_fwd_blend enqueues for these
+ * dimensions, in order.  A profiler can match them to its per-kernel rows,
+ * as the design spec's "nsys Breakdown" table does for the pages' kernels.
+ * A test can use it to check that every launch form the dispatcher can
+ * choose is run against a reference.
+ *
+ * A history too long for its few samples to fill the GPU is cut into
+ * chunks.  The chunks run in parallel: a summary pass, then the carry
+ * across chunks, then the replay pass.  Otherwise one full pass does
+ * everything.  The plan does not depend on the trunk precision.
+ *
+ * Fills launches[0 .. min(n, max_launches) - 1] and returns n (1 or 3), or
+ * a negative status for invalid or unsupported dimensions.  `launches` may
+ * be NULL when max_launches is 0.
+ */
+#define MAMBA2_SCAN_KERNEL_FWD    0 /* projections, gated scan, saved terms  */
+#define MAMBA2_SCAN_KERNEL_CARRY  1 /* carry of the state across chunks      */
+#define MAMBA2_SCAN_PASS_FULL     0 /* whole history: context + saved terms  */
+#define MAMBA2_SCAN_PASS_SUMMARY  1 /* per chunk: gate product, end state    */
+#define MAMBA2_SCAN_PASS_CARRY    2 /* each chunk's start state              */
+#define MAMBA2_SCAN_PASS_REPLAY   3 /* per chunk from its start state        */
+typedef struct {
+  int kernel;        /* MAMBA2_SCAN_KERNEL_*                                 */
+  int sample_blocks; /* 16-sample blocks per work-group (0 for the carry)    */
+  int pass;          /* MAMBA2_SCAN_PASS_*                                   */
+  int chunks;        /* history chunks run in parallel (1: not chunked)      */
+  int chunk_steps;   /* steps per chunk (the last chunk takes the rest)      */
+  int grid;          /* work-groups                                          */
+  int threads;       /* threads per work-group                               */
+} mamba2_scan_launch;
+int mamba2_scan_fwd_plan(int B, int K, int SH2, int STATE_D,
+                         mamba2_scan_launch* launches, int max_launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -268,8 +268,3 @@ def fwd_bwd(inputs: dict):
     b = backward(f, inputs["h_history"], inputs["h_s2"], inputs["d_context"])
     return f, b
 
-
-def loss(h_history, h_s2, W_A, W_B, W_C, d_context) -> float:
-    """The scalar L = sum(d_context * context) whose gradients backward() returns."""
-    f = forward(h_history, h_s2, W_A, W_B, W_C)
-    return float(np.sum(_f64(d_context) * f.context))

@@ -24,7 +24,7 @@ def test_exports_every_header_symbol(L):
         "mamba2_scan_bwd", "mamba2_scan_bwd_partials", "mamba2_scan_bwd_reduce", "mamba2_scan_bwd_input",
         "mamba2_scan_fwd_blend", "mamba2_scan_bwd_blend_workspace_bytes", "mamba2_scan_bwd_blend",
         "mamba2_scan_fwd_bf16", "mamba2_scan_bwd_bf16", "mamba2_scan_bwd_partials_bf16",
-        "mamba2_scan_strerror",
+        "mamba2_scan_strerror", "mamba2_scan_fwd_plan",
     }
     for n in names:
         assert hasattr(L, n), n

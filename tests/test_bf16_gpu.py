@@ -17,7 +17,8 @@ import torch
 import bwd_mamba2_scan_amd as m2
 from oracle import mamba2_oracle as orc
 from tests.inputs import bf16_round, make_inputs, workload_inputs
-from tests.test_parity_gpu import EDGE_SHAPES, assert_elementwise, assert_l1
+from tests.shapes import BF16_CHUNKED_SHAPES, BF16_WORKLOADS, EDGE_SHAPES, FORM_SHAPES, gate_bias
+from tests.test_parity_gpu import assert_elementwise, assert_l1
 
 pytestmark = pytest.mark.gpu
 
@@ -74,21 +75,27 @@ def test_bf16_edge_shapes(B, K, SH2, D):
     check(make_inputs(B, K, SH2, D, seed=B * 3 + K + 2))
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "pages_shape"])
+@pytest.mark.parametrize("name", BF16_WORKLOADS[:3])
 def test_bf16_workloads(name):
     check(workload_inputs(name), debug=(name != "pages_shape"))
 
 
-@pytest.mark.parametrize("name", ["long_history", "wide_state"])
+@pytest.mark.parametrize("name", BF16_WORKLOADS[3:])
 def test_bf16_large(name):
     check(workload_inputs(name), debug=False)
 
 
-@pytest.mark.parametrize("B,K,SH2,D", [(64, 1024, 256, 16), (3, 300, 64, 64), (17, 160, 192, 16)],
-                         ids=lambda v: str(v))
+@pytest.mark.parametrize("B,K,SH2,D", BF16_CHUNKED_SHAPES, ids=lambda v: str(v))
 def test_bf16_chunked_history(B, K, SH2, D):
     """Few samples, long histories: the chunked forward (summary, carry, replay) with bf16 inputs."""
     check(make_inputs(B, K, SH2, D, seed=B + K + 5, gate_bias=2.0), debug=(K <= 300))
+
+
+@pytest.mark.parametrize("B,K,SH2,D", FORM_SHAPES, ids=lambda v: str(v))
+def test_bf16_launch_forms(B, K, SH2, D):
+    """The wide-trunk launch forms (two-block full and summary passes, one-block
+    summary passes, two-block replays) with bf16 inputs."""
+    check(make_inputs(B, K, SH2, D, seed=B + 3 * K + SH2 + 1, gate_bias=gate_bias(K)))
 
 
 def test_bf16_split_phase_matches():

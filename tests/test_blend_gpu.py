@@ -15,7 +15,8 @@ import torch
 import bwd_mamba2_scan_amd as m2
 from oracle import mamba2_oracle as orc
 from tests.inputs import blend_extras, make_inputs, workload_inputs
-from tests.test_parity_gpu import EDGE_SHAPES, _to_dev, assert_elementwise, assert_l1
+from tests.shapes import EDGE_SHAPES
+from tests.test_parity_gpu import _to_dev, assert_elementwise, assert_l1
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +60,16 @@ def check_blend(inputs, extras, m, with_w, rows=None):
 def test_blend_edge_shapes(B, K, SH2, D, m, with_w):
     seed = B * 5 + K
     check_blend(make_inputs(B, K, SH2, D, seed=seed), blend_extras(B, SH2, seed), m, with_w)
+
+
+# The blend fused into the wide-trunk forms at one state group: a two-block
+# full pass (257 pairs of blocks) and a two-block replay after a one-block
+# summary pass.
+@pytest.mark.parametrize("B,K,SH2,D", [(8200, 2, 320, 16), (20, 96, 384, 16)], ids=lambda v: str(v))
+def test_blend_launch_forms(B, K, SH2, D):
+    seed = B + K + 11
+    check_blend(make_inputs(B, K, SH2, D, seed=seed, gate_bias=2.0 if K >= 32 else 0.0),
+                blend_extras(B, SH2, seed), 0.9, True)
 
 
 @pytest.mark.parametrize("name,m", [("tiny", 1.1), ("mid", 0.8), ("pages_shape", 0.95)])

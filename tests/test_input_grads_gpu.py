@@ -15,7 +15,8 @@ import torch
 import bwd_mamba2_scan_amd as m2
 from oracle import mamba2_oracle as orc
 from tests.inputs import make_inputs, workload_inputs
-from tests.test_parity_gpu import EDGE_SHAPES, LONG_FEW_SHAPES, _to_dev, assert_elementwise
+from tests.shapes import EDGE_SHAPES, LONG_FEW_SHAPES
+from tests.test_parity_gpu import _to_dev, assert_elementwise
 
 pytestmark = pytest.mark.gpu
 

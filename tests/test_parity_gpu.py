@@ -18,6 +18,7 @@ import torch
 import bwd_mamba2_scan_amd as m2
 from oracle import mamba2_oracle as orc
 from tests.inputs import WORKLOADS, make_inputs, workload_inputs
+from tests.shapes import EDGE_SHAPES, FORM_SHAPES, FP32_WORKLOADS, LONG_FEW_SHAPES, gate_bias
 
 pytestmark = pytest.mark.gpu
 
@@ -79,40 +80,17 @@ def check_against_oracle(inputs, debug=True):
     return got, f, b
 
 
-# Shapes chosen to cover: one sample, ragged batches (B % 16 != 0), K = 1,
-# K across the 8-step projection rounds (9, 17, 64, 80, 100), every SH2 multiple of 64
-# from 64 to 512, all three state widths, and partial slices in the backward.
-EDGE_SHAPES = [
-    (1, 1, 64, 16),
-    (1, 8, 256, 16),
-    (17, 3, 128, 16),
-    (33, 9, 256, 16),
-    (5, 17, 192, 32),
-    (40, 8, 320, 64),
-    (16, 8, 512, 64),
-    (100, 2, 448, 16),
-    (64, 64, 256, 16),
-    (3, 8, 384, 32),
-    (250, 5, 64, 64),
-    (129, 1, 512, 32),
-    (300, 12, 256, 16),
-    (20, 80, 64, 16),     # ten 8-step rounds: two beyond those held in registers
-    (5, 100, 128, 32),
-    (7, 20, 128, 64),     # four state groups over three rounds
-]
-
-
 @pytest.mark.parametrize("B,K,SH2,D", EDGE_SHAPES, ids=lambda v: str(v))
 def test_edge_shapes(B, K, SH2, D):
     check_against_oracle(make_inputs(B, K, SH2, D, seed=B * 7 + K))
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "pages_shape"])
+@pytest.mark.parametrize("name", FP32_WORKLOADS[:3])
 def test_workload_full(name):
     check_against_oracle(workload_inputs(name), debug=(name != "pages_shape"))
 
 
-@pytest.mark.parametrize("name", ["long_history", "wide_state", "long_few"])
+@pytest.mark.parametrize("name", FP32_WORKLOADS[3:])
 def test_workload_large(name):
     got, f, _ = check_against_oracle(workload_inputs(name), debug=False)
     if name in ("long_history", "long_few"):
@@ -263,27 +241,19 @@ def test_graph_replays_match_eager(B, K, SH2, D, bf16):
             assert np.array_equal(out[k].cpu().numpy().view(np.uint32), eager[k].view(np.uint32)), (rep, k)
 
 
-# Long histories with few samples: the forward splits the history into chunks
-# that run in parallel (summary pass, carry across chunks, full pass).  Shapes
-# chosen so the chunked path is taken, with long-memory gates (+2 logit shift)
-# so that carries across chunk boundaries matter.
-LONG_FEW_SHAPES = [
-    (64, 1024, 256, 16),
-    (8, 2048, 128, 32),
-    (3, 300, 64, 64),
-    (17, 160, 192, 16),
-    (5, 8192, 64, 16),    # one sample block: 512 history chunks, the carry's 32 segments
-    (20, 96, 384, 16),    # a wide trunk in chunks: one-block summary pass, two-block replay
-    (32, 2024, 256, 16),  # 63 chunks of 32 steps, the remainder merged into a 40-step last chunk
-    (32, 2040, 256, 16),  # 64 chunks, the last one 24 steps
-]
-
-
 @pytest.mark.parametrize("B,K,SH2,D", LONG_FEW_SHAPES, ids=lambda v: str(v))
 def test_chunked_history(B, K, SH2, D):
     inputs = make_inputs(B, K, SH2, D, seed=B + K, gate_bias=2.0)
     got, f, _ = check_against_oracle(inputs, debug=True)
     assert 0.8 < float(np.mean(f.g)) < 0.95  # long memory: the carry spans many chunks
+
+
+@pytest.mark.parametrize("B,K,SH2,D", FORM_SHAPES, ids=lambda v: str(v))
+def test_launch_forms(B, K, SH2, D):
+    """The forward launch forms of wide trunks (two sample blocks per work-group,
+    one-block summary passes, two-block replays), each against the oracle."""
+    inputs = make_inputs(B, K, SH2, D, seed=B + 3 * K + SH2, gate_bias=gate_bias(K))
+    check_against_oracle(inputs, debug=True)
 
 
 def test_chunked_history_blend_and_input_grads():
