@@ -9,12 +9,15 @@ Cold protocol (the headline): R input sets rotate so that no step's reads
 can be served from the 256 MB Infinity Cache.  Step s runs the forward of
 set s % R and the backward of set (s - R/2) % R, so between a set's forward
 and its backward R/2 other steps stream far more than the cache holds.
-The K timed steps are replays of captured HIP graphs (a whole number of
-rotations per graph, up to 200 steps, plus one graph for the remainder),
-bracketed by device synchronisation.  A graph's first replay costs more
-than later ones (about 3 us per step for 200 steps), so after the W warmup
-steps each timed graph is replayed once untimed; that replay's time is
-reported as first_replay_ms_per_step.
+The K timed steps are one captured HIP graph of exactly K steps (steps
+0..K-1 of the rotation), timed with HIP events on the stream it is
+replayed on and bracketed by device synchronisation, so the figure does not
+depend on K.  A graph's first replay costs more than later ones (about 3 us
+per step), so after the W warmup steps the timed graph is replayed once
+untimed; that replay's time is reported as first_replay_ms_per_step.
+
+Warm protocol (secondary): K steps of fwd then bwd of one set, back to back
+in one graph, so the backward may find the batch in the Infinity Cache.
 
 Per-kernel durations come from HIP events (on the stream the kernels run on)
 around a captured batch of back-to-back launches of one kernel that walks the
@@ -41,7 +44,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
 SRC = os.path.join(ROOT, "bwd_mamba2_scan_amd", "csrc", "mamba2_scan.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pages_shape.json")
-MAX_GRAPH_STEPS = 200  # steps per captured graph in the timed region
+MAX_STEPS = 2000  # steps of the one captured graph that is timed
 BLEND_STABILITY = 0.95  # the blend measurement's gate multiplier
 
 
@@ -183,6 +186,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the blend, bf16 and long_few measurements (keeps a profile to the headline kernels)")
     args = ap.parse_args()
+    if not 1 <= args.steps <= MAX_STEPS or args.warmup < 0:
+        ap.error(f"--steps must be in 1..{MAX_STEPS} and --warmup >= 0")
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scan's batch shards with no communication in the "
@@ -285,41 +290,41 @@ def main():
         for i in range(n % R):
             graphs[i].replay()
 
-    # The timed steps run as few graph replays as possible: one graph holds a
-    # whole number of rotations (up to MAX_GRAPH_STEPS steps), a second one the
-    # remainder, so the host's per-replay launch gap does not enter the step time.
-    def capture(count):
+    # The K timed steps are one captured graph of exactly K steps (steps
+    # 0..K-1 of the rotation), so the host's per-launch gaps stay out
+    # and the figure does not depend on how K splits into graphs.  A graph's
+    # first replay costs more than later ones (about 3 us per step), so it is
+    # replayed once untimed after the warm-up; the timed replay is bracketed
+    # by device synchronisations and timed with HIP events on its stream.
+    def capture(count, fn):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             with torch.cuda.graph(g, stream=stream):
                 for i in range(count):
-                    step(i)
+                    fn(i)
         return g
 
-    chunk = min(max(R, (args.steps // R) * R), MAX_GRAPH_STEPS)
-    big = capture(chunk)
-    n_big, rem = divmod(args.steps, chunk)
-    rest = capture(rem) if rem else None
-    torch.cuda.synchronize()
+    def timed_replay(g):
+        """(event ms, wall ms) of one replay, synchronised on both sides."""
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3
 
+    timed = capture(args.steps, step)
+    torch.cuda.synchronize()
     run_steps(args.warmup)
-    torch.cuda.synchronize()
-    # first replay of each timed graph, untimed (one-time launch cost)
-    tf = time.perf_counter()
-    big.replay()
-    if rest is not None:
-        rest.replay()
-    torch.cuda.synchronize()
-    first_ms = (time.perf_counter() - tf) * 1e3 / (chunk + rem)
-    t0 = time.perf_counter()
-    for _ in range(n_big):
-        big.replay()
-    if rest is not None:
-        rest.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    del big, rest
+    first_ev, _ = timed_replay(timed)  # first replay, untimed for the headline
+    ev_ms, wall_ms = timed_replay(timed)
+    ms_per_step = ev_ms / args.steps
+    first_ms = first_ev / args.steps
+    del timed
 
     # ---- spread: one event pair per rotation replay (R steps each)
     rot_ms = []
@@ -334,22 +339,19 @@ def main():
             rot_ms.append(e0.elapsed_time(e1) / R)
     step_pct = {k: round(float(np.percentile(rot_ms, q)), 5) for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
 
-    # ---- warm protocol (secondary): fwd then bwd of the same set, back to back
-    warm_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(warm_graph, stream=stream):
-            fwd(sets[0])
-            partials(sets[0])
-            reduce(sets[0])
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        warm_graph.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        warm_graph.replay()
-    torch.cuda.synchronize()
-    warm_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    # ---- warm protocol (secondary): K steps of fwd then bwd of the same set,
+    # back to back in one graph, so the backward may read the batch from the
+    # Infinity Cache
+    def warm_step(i):
+        fwd(sets[0])
+        partials(sets[0])
+        reduce(sets[0])
+
+    warm_graph = capture(args.steps, warm_step)
+    timed_replay(warm_graph)
+    warm_ev, _ = timed_replay(warm_graph)
+    warm_ms = warm_ev / args.steps
+    del warm_graph
 
     # ---- per-kernel durations: HIP events around each kernel, cold rotation,
     # eager launches on the current stream (the one the kernels run on)
@@ -535,8 +537,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload, "B": B, "K": K, "SH2": SH2, "STATE_D": D,
-            "protocol": f"cold: {R} rotating input sets, fwd(set s) + bwd(set s-{R // 2}) per step, "
-                        f"timed steps replayed from HIP graphs of up to {MAX_GRAPH_STEPS} steps",
+            "protocol": f"cold: {R} rotating input sets, fwd(set s) + bwd(set s-{R // 2}) per step; "
+                        f"the {args.steps} timed steps are one HIP graph, replayed once untimed, then timed "
+                        f"with HIP events",
         },
         "hbm_roofline_frac": round(hbm_us / (ms_per_step * 1e3), 4),
         "roofline_frac_step": round(roofline_us / (ms_per_step * 1e3), 4),
@@ -548,6 +551,7 @@ def main():
         "step_ms_per_rotation": step_pct,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "achieved_over_copy_ceiling": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / copy_gbps, 4),
+        "wall_ms_per_step": round(wall_ms / args.steps, 5),
         "warm_ms_per_step": round(warm_ms, 5),
         "first_replay_ms_per_step": round(first_ms, 5),
         "kernel_us": {n: round(kern_us[n], 2) for n in names},

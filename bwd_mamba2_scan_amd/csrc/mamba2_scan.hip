@@ -48,6 +48,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+
 #include "mamba2_scan.h"
 
 typedef float v4f __attribute__((ext_vector_type(4)));

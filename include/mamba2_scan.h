@@ -87,13 +87,24 @@ int mamba2_scan_fwd(int B, int K, int SH2, int STATE_D,
 /*
  * Backward (plan Task 2; design spec backward steps 1-3).
  *   h_history, h_s2       the same buffers the forward read           (in)
- *   saved                 the forward's `saved` for those inputs      (in)
+ *   saved                 the forward's `saved` for those inputs      (in,
+ *                         required: NULL returns MAMBA2_SCAN_ENULL)
  *   d_context [B][STATE_D] upstream gradient dL/dcontext              (in)
  *   dW_A, dW_B, dW_C [SH2][STATE_D]                                   (out)
  *   d_a, d_b [B][K][STATE_D], d_c [B][STATE_D]  optional (out); NULL skips
  *   workspace             workspace_bytes >= mamba2_scan_bwd_workspace_bytes
  * Equivalent to mamba2_scan_bwd_partials followed by mamba2_scan_bwd_reduce
  * on the same stream.  The weight gradients are bitwise reproducible.
+ *
+ * Why `saved` is required: the two pages differ on where the backward gets
+ * the projections.  The plan's Task 2 step 4 reuses the forward's A/B
+ * projections, which the forward saves.  The spec's backward step 1 replays
+ * them from h_history.  Both give the same results.  This library takes the
+ * plan's reading.  The forward stores per-step gate coefficients (8.5 MiB at
+ * B=8192, K=8, SH2=256, STATE_D=16), and the backward reads them instead of
+ * projecting H a second time.  That second projection would add a whole
+ * contraction to a kernel that already streams H through its matrix cores.
+ * No replay form is offered, so `saved` cannot be NULL.
  */
 int mamba2_scan_bwd(int B, int K, int SH2, int STATE_D,
                     const float* h_history, const float* h_s2,
@@ -206,7 +217,11 @@ int mamba2_scan_bwd_blend(int B, int K, int SH2, int STATE_D,
 /*
  * Reduced-precision trunk inputs: h_history and h_s2 hold bfloat16 values
  * (their 16-bit patterns, the top half of the fp32 with the same value),
- * halving the bytes of the dominant reads.  The bf16 values meet bf16
+ * halving the bytes of the dominant reads.  The xtrain page "Phase T7:
+ * Performance -- Design Document", section "Follow-up" item 4 (bf16 mixed
+ * precision with an fp32 master copy), defers this idea: bf16 matmuls change
+ * the numerics and would need their own, wider tolerance.  Here only the
+ * storage is bf16.  The bf16 values meet bf16
  * matrix instructions whose other operand (the weights in the forward,
  * d_a/d_b/d_c in the backward) is split exactly into three bf16 terms, so
  * every product is exact in fp32 and every sum accumulates in fp32: results
