@@ -2,8 +2,7 @@
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 16] [--workload pages_shape] [--no-extras]
 
-One step = mamba2_scan_fwd + mamba2_scan_bwd (partials + reduce) over one
-batch of seeded synthetic input already resident in HBM.  Prints one JSON line.
+One step = mamba2_scan_fwd + mamba2_scan_bwd over one batch of seeded synthetic input already resident in HBM.  Prints one JSON line.
 
 Cold protocol (the headline): R input sets rotate so that no step's reads
 can be served from the 256 MB Infinity Cache.  Step s runs the forward of
@@ -219,7 +218,7 @@ def main():
         s["context"] = torch.empty((B, D), device=dev)
         s["saved"] = m2.alloc_saved(B, K, SH2, D, dev)
         s["ws"] = m2.alloc_workspace(B, K, SH2, D, dev)
-        s["dW"] = [torch.empty((SH2, D), device=dev) for _ in range(3)]
+        s["dWd"] = {k: torch.empty((SH2, D), device=dev) for k in ("dW_A", "dW_B", "dW_C")}
         s["dH"] = torch.empty((B, K, SH2), device=dev)
         s["dhs2"] = torch.empty((B, SH2), device=dev)
         # the h_enriched blend (an optional step after the path)
@@ -237,11 +236,15 @@ def main():
     def fwd(s):
         m2.fwd(s["h_history"], s["h_s2"], s["W_A"], s["W_B"], s["W_C"], context=s["context"], saved=s["saved"])
 
+    def bwd(s):
+        m2.bwd(s["h_history"], s["h_s2"], s["saved"], s["d_context"], workspace=s["ws"], out=s["dWd"])
+
+    # the backward's two kernels, each timed on its own
     def partials(s):
         m2.bwd_partials(s["h_history"], s["h_s2"], s["saved"], s["d_context"], s["ws"])
 
     def reduce(s):
-        m2.bwd_reduce(B, K, SH2, D, s["ws"], *s["dW"])
+        m2.bwd_reduce(B, K, SH2, D, s["ws"], s["dWd"]["dW_A"], s["dWd"]["dW_B"], s["dWd"]["dW_C"])
 
     def fwd_blend(s):
         m2.fwd_blend(s["h_history"], s["h_s2"], s["W_A"], s["W_B"], s["W_C"], stability=s["stab"],
@@ -258,8 +261,7 @@ def main():
     def step(i):
         fwd(sets[i % R])
         sb = sets[(i - R // 2) % R]
-        partials(sb)
-        reduce(sb)
+        bwd(sb)
 
     # prime every set's saved buffer so the first backwards read real data
     for s in sets:
@@ -344,8 +346,7 @@ def main():
     # Infinity Cache
     def warm_step(i):
         fwd(sets[0])
-        partials(sets[0])
-        reduce(sets[0])
+        bwd(sets[0])
 
     warm_graph = capture(args.steps, warm_step)
     timed_replay(warm_graph)
@@ -416,14 +417,13 @@ def main():
     def fwd16(s):
         m2.fwd(s["h16"], s["hs16"], s["W_A"], s["W_B"], s["W_C"], context=s["context"], saved=s["saved"])
 
-    def partials16(s):
-        m2.bwd_partials(s["h16"], s["hs16"], s["saved"], s["d_context"], s["ws"])
+    def bwd16(s):
+        m2.bwd(s["h16"], s["hs16"], s["saved"], s["d_context"], workspace=s["ws"], out=s["dWd"])
 
     def step16(i):
         fwd16(sets[i % R])
         sb = sets[(i - R // 2) % R]
-        partials16(sb)
-        reduce(sb)
+        bwd16(sb)
 
     # ---- a long history with few samples (chunked forward), its own rotation
     def workload_step_us(name):
@@ -435,7 +435,7 @@ def main():
             x["context"] = torch.empty((wl.B, wl.D), device=dev)
             x["saved"] = m2.alloc_saved(wl.B, wl.K, wl.SH2, wl.D, dev)
             x["ws"] = m2.alloc_workspace(wl.B, wl.K, wl.SH2, wl.D, dev)
-            x["dW"] = [torch.empty((wl.SH2, wl.D), device=dev) for _ in range(3)]
+            x["dWd"] = {k: torch.empty((wl.SH2, wl.D), device=dev) for k in ("dW_A", "dW_B", "dW_C")}
             wsets.append(x)
         del base_in
 
@@ -443,8 +443,8 @@ def main():
             a = wsets[i % R]
             m2.fwd(a["h_history"], a["h_s2"], a["W_A"], a["W_B"], a["W_C"], context=a["context"], saved=a["saved"])
             bset = wsets[(i - R // 2) % R]
-            m2.bwd_partials(bset["h_history"], bset["h_s2"], bset["saved"], bset["d_context"], bset["ws"])
-            m2.bwd_reduce(wl.B, wl.K, wl.SH2, wl.D, bset["ws"], *bset["dW"])
+            m2.bwd(bset["h_history"], bset["h_s2"], bset["saved"], bset["d_context"], workspace=bset["ws"],
+                   out=bset["dWd"])
 
         for i in range(R):
             a = wsets[i]
@@ -468,7 +468,7 @@ def main():
             st_["hs16"] = st_["h_s2"].to(torch.bfloat16)
         bf16_step_us = graph_us(step16, R)
         bf16_kern_us = {"fwd_kernel": graph_us(lambda i: fwd16(sets[i % R]), 8 * R),
-                        "bwd_partials_kernel": graph_us(lambda i: partials16(sets[i % R]), 8 * R)}
+                        "bwd": graph_us(lambda i: bwd16(sets[i % R]), 8 * R)}
         for st_ in sets:
             del st_["h16"], st_["hs16"]
         if args.workload == "pages_shape":
