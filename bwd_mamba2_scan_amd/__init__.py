@@ -30,6 +30,7 @@ ENULL = -3
 ESIZE = -4
 EALIGN = -5
 EHIP = -6
+ESCRATCH = -7
 
 
 class Mamba2ScanError(RuntimeError):
@@ -60,6 +61,7 @@ _SIGNATURES = {
     "mamba2_scan_bwd_partials_bf16": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 5 + [_c_size, _c_vp]),
     "mamba2_scan_strerror": (ctypes.c_char_p, [_c_int]),
     "mamba2_scan_fwd_plan": (_c_int, [_c_int] * 4 + [_c_vp, _c_int]),
+    "mamba2_scan_bwd_noalloc": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 8),
 }
 
 

@@ -48,6 +48,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "mamba2_scan.h"
 
@@ -2050,6 +2051,51 @@ void launch_dinput(const Plan& pl, const float* WA, const float* WB, const float
                        pl.NB, upw, WA, WB, WC, sv, dctx, dH, dhs2);
 }
 
+// Scratch for callers that cannot allocate (mamba2_scan_bwd_noalloc): the
+// backward's split-K slices live here instead of in a caller workspace.
+// Every supported shape needs at most ~3.3 MiB of slices (about 256 slices
+// of SH2 x 48 floats per state group, fewer as SH2 * STATE_D grows).  Each
+// device holds its own copy until the process ends; calls on one device
+// share it.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (the host-side name is a stand-in, not a
+// device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MAMBA2_SCAN_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MAMBA2_SCAN_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MAMBA2_SCAN_OK;
+}
+
+// The argument checks of mamba2_scan_bwd, less the workspace (the no-alloc
+// backward brings its own): all of them run before the scratch address is
+// looked up, so a bad call returns without touching the device.
+int check_bwd_noalloc(const Plan& pl, const void* H, const void* hs2, const void* saved, size_t saved_bytes,
+                      const float* dctx, const float* dWA, const float* dWB, const float* dWC, const float* da,
+                      const float* db, const float* dc) {
+  if (!H || !hs2 || !saved || !dctx || !dWA || !dWB || !dWC) return MAMBA2_SCAN_ENULL;
+  if (saved_bytes < pl.saved_bytes) return MAMBA2_SCAN_ESIZE;
+  if (pl.ws_bytes > kScratchBytes) return MAMBA2_SCAN_ESCRATCH;
+  if (!aligned16(H) || !aligned16(hs2) || !aligned16(saved) || !aligned4(dctx) || !aligned4(dWA) ||
+      !aligned4(dWB) || !aligned4(dWC))
+    return MAMBA2_SCAN_EALIGN;
+  if ((da && !aligned4(da)) || (db && !aligned4(db)) || (dc && !aligned4(dc))) return MAMBA2_SCAN_EALIGN;
+  return MAMBA2_SCAN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2138,6 +2184,21 @@ int mamba2_scan_bwd(int B, int K, int SH2, int STATE_D, const float* h_history, 
   if (st != MAMBA2_SCAN_OK) return st;
   launch_reduce(pl, workspace, dW_A, dW_B, dW_C, s);
   return launch_status();
+}
+
+int mamba2_scan_bwd_noalloc(int B, int K, int SH2, int STATE_D, const float* h_history, const float* h_s2,
+                            const void* saved, size_t saved_bytes, const float* d_context, float* dW_A, float* dW_B,
+                            float* dW_C, float* d_a, float* d_b, float* d_c, void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_bwd_noalloc(pl, h_history, h_s2, saved, saved_bytes, d_context, dW_A, dW_B, dW_C, d_a, d_b, d_c);
+  if (st != MAMBA2_SCAN_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MAMBA2_SCAN_OK) return st;
+  return mamba2_scan_bwd(B, K, SH2, STATE_D, h_history, h_s2, saved, saved_bytes, d_context, dW_A, dW_B, dW_C, d_a,
+                         d_b, d_c, ws, kScratchBytes, stream);
 }
 
 int mamba2_scan_fwd_bf16(int B, int K, int SH2, int STATE_D, const void* h_history, const void* h_s2,
@@ -2267,6 +2328,7 @@ const char* mamba2_scan_strerror(int status) {
     case MAMBA2_SCAN_ESIZE: return "saved or workspace buffer is smaller than required";
     case MAMBA2_SCAN_EALIGN: return "pointer misaligned (inputs, saved and workspace need 16 bytes)";
     case MAMBA2_SCAN_EHIP: return "HIP runtime error while enqueuing a kernel";
+    case MAMBA2_SCAN_ESCRATCH: return "the shape needs more scratch than the library's fixed 4 MiB buffer";
     default: return "unknown status";
   }
 }

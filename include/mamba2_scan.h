@@ -52,6 +52,7 @@ extern "C" {
 #define MAMBA2_SCAN_ESIZE        -4 /* saved or workspace buffer too small    */
 #define MAMBA2_SCAN_EALIGN       -5 /* a pointer is not aligned as required   */
 #define MAMBA2_SCAN_EHIP         -6 /* the HIP runtime refused a launch       */
+#define MAMBA2_SCAN_ESCRATCH     -7 /* more scratch than the fixed buffer     */
 
 /*
  * Bytes of the `saved` buffer that mamba2_scan_fwd fills and mamba2_scan_bwd
@@ -114,6 +115,26 @@ int mamba2_scan_bwd(int B, int K, int SH2, int STATE_D,
                     float* d_a, float* d_b, float* d_c,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * mamba2_scan_bwd without a workspace, for callers that cannot allocate
+ * device memory: code under stream capture, tight serving loops, harnesses
+ * that forbid it.  The split-K slices go to a fixed 4 MiB buffer inside the
+ * library, one per device, which every supported shape fits.  A shape that
+ * needed more would return MAMBA2_SCAN_ESCRATCH.  The call allocates nothing.
+ * Its first call on a device looks up that device's buffer, so the device
+ * must be current.  Every call on a device shares its buffer, so calls that
+ * overlap in time on one device (different streams, or concurrent host
+ * threads enqueuing on them) race.  Results match mamba2_scan_bwd bit for
+ * bit.  The other arguments are as for mamba2_scan_bwd.
+ */
+int mamba2_scan_bwd_noalloc(int B, int K, int SH2, int STATE_D,
+                            const float* h_history, const float* h_s2,
+                            const void* saved, size_t saved_bytes,
+                            const float* d_context,
+                            float* dW_A, float* dW_B, float* dW_C,
+                            float* d_a, float* d_b, float* d_c,
+                            void* stream);
 
 /*
  * First phase of the backward: the reverse scan and the split-K products

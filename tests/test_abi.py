@@ -24,14 +24,14 @@ def test_exports_every_header_symbol(L):
         "mamba2_scan_bwd", "mamba2_scan_bwd_partials", "mamba2_scan_bwd_reduce", "mamba2_scan_bwd_input",
         "mamba2_scan_fwd_blend", "mamba2_scan_bwd_blend_workspace_bytes", "mamba2_scan_bwd_blend",
         "mamba2_scan_fwd_bf16", "mamba2_scan_bwd_bf16", "mamba2_scan_bwd_partials_bf16",
-        "mamba2_scan_strerror", "mamba2_scan_fwd_plan",
+        "mamba2_scan_strerror", "mamba2_scan_fwd_plan", "mamba2_scan_bwd_noalloc",
     }
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_strerror_covers_codes():
-    for code in (m2.OK, m2.EBADDIM, m2.EUNSUPPORTED, m2.ENULL, m2.ESIZE, m2.EALIGN, m2.EHIP):
+    for code in (m2.OK, m2.EBADDIM, m2.EUNSUPPORTED, m2.ENULL, m2.ESIZE, m2.EALIGN, m2.EHIP, m2.ESCRATCH):
         assert m2.strerror(code) and m2.strerror(code) != "unknown status"
     assert m2.strerror(12345) == "unknown status"
 
@@ -206,3 +206,25 @@ def test_bf16_entry_points_check_like_fp32(L):
     assert L.mamba2_scan_bwd_bf16(*dims, g, g, g, sv, g, g, g, g, None, None, None, g, ws - 4, None) == m2.ESIZE
     assert L.mamba2_scan_bwd_partials_bf16(*dims, g, ctypes.c_void_p(0x60002), g, sv, g, None, None, None, g, ws,
                                            None) == m2.EALIGN
+
+
+def test_noalloc_argument_checks(L):
+    """The no-alloc backward runs every check before it looks up its buffer (no device needed here)."""
+    dims = (100, 5, 192, 32)
+    sv = m2.saved_bytes(*dims)
+    g = ctypes.c_void_p(0x20000)
+
+    def call(*, dims=dims, h=g, hs=g, saved=g, svb=sv, dctx=g, dwa=g, dwb=g, dwc=g, da=None, db=None, dc=None):
+        return L.mamba2_scan_bwd_noalloc(*dims, h, hs, saved, svb, dctx, dwa, dwb, dwc, da, db, dc, None)
+
+    L.mamba2_scan_bwd_noalloc.restype = ctypes.c_int
+    assert call(dims=(0, 5, 192, 32)) == m2.EBADDIM
+    assert call(dims=(100, 5, 100, 32)) == m2.EUNSUPPORTED
+    for k in ("h", "hs", "saved", "dctx", "dwa", "dwb", "dwc"):
+        assert call(**{k: None}) == m2.ENULL, k
+    assert call(svb=sv - 4) == m2.ESIZE
+    assert call(saved=ctypes.c_void_p(0x20004)) == m2.EALIGN
+    assert call(dwb=ctypes.c_void_p(0x20002)) == m2.EALIGN
+    assert call(da=ctypes.c_void_p(0x20001)) == m2.EALIGN
+    assert m2.strerror(m2.ESCRATCH) != "unknown status"
+
