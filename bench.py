@@ -47,11 +47,12 @@ MAX_STEPS = 2000  # steps of the one captured graph that is timed
 BLEND_STABILITY = 0.95  # the blend measurement's gate multiplier
 
 
-def algorithmic_bytes(B, K, SH2, D):
-    """What the method must move, fwd and bwd as separate calls (fp32)."""
+def algorithmic_bytes(B, K, SH2, D, trunk_bytes=4):
+    """What the method must move, fwd and bwd as separate calls (fp32; the
+    trunk inputs h_history and h_s2 at trunk_bytes per value)."""
     f = 4
-    H = B * K * SH2 * f
-    hs2 = B * SH2 * f
+    H = B * K * SH2 * trunk_bytes
+    hs2 = B * SH2 * trunk_bytes
     W = 3 * SH2 * D * f
     vec = B * D * f
     fwd = H + hs2 + W + vec          # read H, h_s2, W_A/B/C; write context
@@ -143,7 +144,7 @@ def cpu_baseline(workload_name, budget_s=12.0):
     return out
 
 
-def parity_gate(m2, torch, t, inputs):
+def parity_gate(m2, torch, t, inputs, input_grads=True):
     """Oracle parity on the benchmarked workload before any timing."""
     from oracle import mamba2_oracle as orc
 
@@ -159,13 +160,14 @@ def parity_gate(m2, torch, t, inputs):
         rel = float(np.sum(np.abs(g[k].cpu().numpy() - ref)) / np.sum(np.abs(ref)))
         worst_l1 = max(worst_l1, rel)
         ok = ok and rel <= 1e-3
-    dH, dhs2 = m2.bwd_input(t["W_A"], t["W_B"], t["W_C"], saved, t["d_context"], inputs["h_history"].shape[1])
-    torch.cuda.synchronize()
-    ig = orc.input_grads(b, inputs["W_A"], inputs["W_B"], inputs["W_C"])
     in_err = 0.0
-    for got, ref in ((dH, ig.d_h_history), (dhs2, ig.d_h_s2)):
-        v = got.cpu().numpy().astype(np.float64)
-        in_err = max(in_err, float(np.max(np.abs(v - ref) / (1 + np.abs(ref)))))
+    if input_grads:
+        dH, dhs2 = m2.bwd_input(t["W_A"], t["W_B"], t["W_C"], saved, t["d_context"], inputs["h_history"].shape[1])
+        torch.cuda.synchronize()
+        ig = orc.input_grads(b, inputs["W_A"], inputs["W_B"], inputs["W_C"])
+        for got, ref in ((dH, ig.d_h_history), (dhs2, ig.d_h_s2)):
+            v = got.cpu().numpy().astype(np.float64)
+            in_err = max(in_err, float(np.max(np.abs(v - ref) / (1 + np.abs(ref)))))
     ok = ok and in_err <= 1e-4
     if not ok:
         raise SystemExit(f"parity gate failed on the benchmarked workload (worst dW L1 {worst_l1:.3e}, "
@@ -181,6 +183,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="pages_shape")
     ap.add_argument("--sets", type=int, default=8, help="rotating input sets (even, >= 2)")
+    ap.add_argument("--trunk", choices=("fp32", "bf16"), default="fp32",
+                    help="storage of h_history and h_s2 (bf16: the *_bf16 entry points; the headline is fp32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the blend, bf16 and long_few measurements (keeps a profile to the headline kernels)")
@@ -209,6 +213,16 @@ def main():
     extras = blend_extras(B, SH2, w.seed)
     base = {k: torch.from_numpy(v).to(dev) for k, v in inputs.items()}
     gate = parity_gate(m2, torch, base, inputs)
+    tb = 2 if args.trunk == "bf16" else 4
+    if args.trunk == "bf16":
+        # the trunk inputs as bf16 (the forward and backward read them as such);
+        # the oracle runs on the same rounded values
+        from tests.inputs import bf16_round
+        rounded = dict(inputs)
+        for k in ("h_history", "h_s2"):
+            bits, rounded[k] = bf16_round(inputs[k])
+            base[k] = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        gate["bf16"] = parity_gate(m2, torch, base, rounded, input_grads=False)
 
     # R distinct copies of the batch at distinct addresses, each with its own
     # context/saved/workspace/dW buffers.
@@ -461,7 +475,7 @@ def main():
     blend_step_us = bf16_step_us = None
     bf16_kern_us = {}
     long_few = None
-    if not args.no_extras:
+    if not args.no_extras and args.trunk == "fp32":
         blend_step_us = graph_us(blend_step, R)
         for st_ in sets:
             st_["h16"] = st_["h_history"].to(torch.bfloat16)
@@ -491,7 +505,7 @@ def main():
     copy_gbps = 2 * src.numel() * 4 / (min(copy_ms[1:]) * 1e-3) / 1e9
     del src, dst
 
-    step_bytes, per_kernel_bytes = algorithmic_bytes(B, K, SH2, D)
+    step_bytes, per_kernel_bytes = algorithmic_bytes(B, K, SH2, D, tb)
     # bf16 trunk inputs: h_history and h_s2 move half the bytes, twice per step
     bf16_bytes = step_bytes - (B * K * SH2 + B * SH2) * 4
     blend_out = bf16_out = None
@@ -520,7 +534,7 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(per_kernel_bytes[dom] / (kern_us[dom] * 1e-6) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dom) if args.workload == "pages_shape" else None
+    roof["traffic"] = measured_traffic(dom) if (args.workload, args.trunk) == ("pages_shape", "fp32") else None
 
     out = {
         "metric": METRIC,
@@ -536,7 +550,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": args.workload, "B": B, "K": K, "SH2": SH2, "STATE_D": D,
+            "workload": args.workload, "B": B, "K": K, "SH2": SH2, "STATE_D": D, "trunk": args.trunk,
             "protocol": f"cold: {R} rotating input sets, fwd(set s) + bwd(set s-{R // 2}) per step; "
                         f"the {args.steps} timed steps are one HIP graph, replayed once untimed, then timed "
                         f"with HIP events",
@@ -568,7 +582,8 @@ def main():
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(per_kernel_bytes["dinput_kernel"] / (kern_us["dinput_kernel"] * 1e-6) / 1e9
                                       / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic("dinput_kernel") if args.workload == "pages_shape" else None},
+                        "traffic": (measured_traffic("dinput_kernel")
+                                    if (args.workload, args.trunk) == ("pages_shape", "fp32") else None)},
         "parity": gate,
     }
     if not args.no_cpu_baseline:

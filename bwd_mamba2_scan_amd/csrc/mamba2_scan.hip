@@ -288,6 +288,7 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
   const int blk = min(pair * kFwdBlocks + half, NB - 1);
   const int kg = lane >> 4;  // k-group of the A/B operands, row quad of the result
   const int m = lane & 15;   // row of A (sample) / column of B and result (state)
+  const int wlane = lane ^ ((lane >> 3) & 3);  // this lane's slot in a weight-slab pair (swizzled)
 
   // Scan lanes: waves 0..3, lane (i = lane>>4, n = lane&15) owns sample
   // smp = 4*wave + i and state n.
@@ -326,6 +327,11 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
   // W_A, W_B (split terms): a task is (matrix, octet o of rows 8o..8o+7,
   // states 4*s4..4*s4+3), one per thread; per state n it writes the eight
   // rows' three terms as three 16-byte entries (pair o/4, lane (o%4, n)).
+  // Entry l of a pair's 64 sits at slot wsw(l) = l ^ ((l >> 3) & 3): the
+  // LDS serves a 16-byte access 8 lanes per cycle from 128 bytes of banks,
+  // and with that swizzle both the staging writes (lanes 64 bytes apart)
+  // and the operand reads (lane l reads entry l) touch 8 distinct 16-byte
+  // bank groups per 8 lanes.
   // The rows are loaded here and waited for; the split and its LDS writes
   // run after the first history loads have gone out, under their latency.
   constexpr int NTASK = 2 * (SH2 / 8) * 4;  // = SH2
@@ -360,7 +366,8 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
           tm[jj] = mi;
           tl[jj] = (__bf16)r2;
         }
-        const int e = ((o >> 2) * 64 + (o & 3) * 16 + 4 * s4 + q);
+        const int el = (o & 3) * 16 + 4 * s4 + q;  // entry within the pair
+        const int e = (o >> 2) * 64 + (el ^ ((el >> 3) & 3));
         sWab[(mat * 3 + 0) * NP * 64 + e] = __builtin_bit_cast(v4u, th);
         sWab[(mat * 3 + 1) * NP * 64 + e] = __builtin_bit_cast(v4u, tm);
         sWab[(mat * 3 + 2) * NP * 64 + e] = __builtin_bit_cast(v4u, tl);
@@ -582,9 +589,9 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
 #pragma unroll
           for (int tm = 0; tm < 3; ++tm) {
             acca = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                h, __builtin_bit_cast(v8bf, sWab[(0 * 3 + tm) * NP * 64 + pp * 64 + lane]), acca, 0, 0, 0);
+                h, __builtin_bit_cast(v8bf, sWab[(0 * 3 + tm) * NP * 64 + pp * 64 + wlane]), acca, 0, 0, 0);
             accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                h, __builtin_bit_cast(v8bf, sWab[(1 * 3 + tm) * NP * 64 + pp * 64 + lane]), accb, 0, 0, 0);
+                h, __builtin_bit_cast(v8bf, sWab[(1 * 3 + tm) * NP * 64 + pp * 64 + wlane]), accb, 0, 0, 0);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -627,8 +634,8 @@ __global__ __launch_bounds__(NBLK * kFwdWaves * 64) void fwd_kernel(
         // products first; one weight term's operands live at a time
 #pragma unroll
         for (int tw = 2; tw >= 0; --tw) {
-          const v8bf wa = __builtin_bit_cast(v8bf, sWab[(0 * 3 + tw) * NP * 64 + pp * 64 + lane]);
-          const v8bf wb = __builtin_bit_cast(v8bf, sWab[(1 * 3 + tw) * NP * 64 + pp * 64 + lane]);
+          const v8bf wa = __builtin_bit_cast(v8bf, sWab[(0 * 3 + tw) * NP * 64 + pp * 64 + wlane]);
+          const v8bf wb = __builtin_bit_cast(v8bf, sWab[(1 * 3 + tw) * NP * 64 + pp * 64 + wlane]);
 #pragma unroll
           for (int ta = 2 - tw; ta >= 0; --ta) {
             acca = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xt[ta], wa, acca, 0, 0, 0);
