@@ -66,6 +66,9 @@ def algorithmic_bytes(B, K, SH2, D, trunk_bytes=4):
         # optional input gradients: read W and d_context, write d_h_history and d_h_s2
         "dinput_kernel": W + vec + H + hs2,
     }
+    # the backward with the input gradients: its reads and dW writes, plus the
+    # d_h_history and d_h_s2 writes (fp32 whatever the trunk precision)
+    per_kernel["bwd_full"] = bwd + (B * K * SH2 + B * SH2) * f
     # the optional blend step: the scan's bytes plus the h_enriched write (h_s2
     # is read already), the d_h_enriched read (in place of d_context) and the
     # temporal weights (read twice, their gradient written)
@@ -272,6 +275,11 @@ def main():
         m2.bwd_input(s["W_A"], s["W_B"], s["W_C"], s["saved"], s["d_context"], K, d_h_history=s["dH"],
                      d_h_s2=s["dhs2"])
 
+    # the backward with the input gradients in one call
+    def bwd_full(s):
+        m2.bwd_full(s["h_history"], s["h_s2"], s["saved"], s["d_context"], s["W_A"], s["W_B"], s["W_C"],
+                    workspace=s["ws"], out={**s["dWd"], "d_h_history": s["dH"], "d_h_s2": s["dhs2"]})
+
     def step(i):
         fwd(sets[i % R])
         sb = sets[(i - R // 2) % R]
@@ -472,6 +480,11 @@ def main():
                 "algorithmic_bytes": wbytes, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBS, 4)}
 
+    # the backward with the input gradients: one call against the two separate
+    # calls, each a cold rotation replayed from one captured graph
+    full_us = graph_us(lambda i: bwd_full(sets[i % R]), 8 * R)
+    sep_us = graph_us(lambda i: (bwd(sets[i % R]), dinput(sets[i % R])), 8 * R)
+
     blend_step_us = bf16_step_us = None
     bf16_kern_us = {}
     long_few = None
@@ -577,6 +590,13 @@ def main():
         "bf16_step": bf16_out,
         # not part of the step either: the blend path, fwd_blend + bwd_blend, cold rotation
         "blend_step": blend_out,
+        # the backward with the input gradients (mamba2_scan_bwd_full) against
+        # mamba2_scan_bwd followed by mamba2_scan_bwd_input
+        "bwd_full": {"us": round(full_us, 2), "separate_us": round(sep_us, 2),
+                     "algorithmic_bytes": per_kernel_bytes["bwd_full"],
+                     "achieved": round(per_kernel_bytes["bwd_full"] / (full_us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(per_kernel_bytes["bwd_full"] / (full_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "input_grads": {"kernel": "dinput_kernel", "us": round(kern_us["dinput_kernel"], 2), "bound": "hbm",
                         "achieved": round(per_kernel_bytes["dinput_kernel"] / (kern_us["dinput_kernel"] * 1e-6) / 1e9, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",

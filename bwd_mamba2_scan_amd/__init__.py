@@ -10,6 +10,7 @@ The entry points mirror include/mamba2_scan.h:
     bwd(h_history, h_s2, saved, d_context)      -> dict(dW_A, dW_B, dW_C[, d_a, d_b, d_c])
     bwd_partials(...), bwd_reduce(...)          -- the two phases of bwd
     bwd_input(W_A, W_B, W_C, saved, d_context, K) -> (d_h_history, d_h_s2)
+    bwd_full(h_history, h_s2, saved, d_context, W_A, W_B, W_C) -> dict(dW_*, d_h_history, d_h_s2)
     fwd_blend(...) -> (context, h_enriched, saved);  bwd_blend(...) -> dict(...)
     saved_bytes(B, K, SH2, D), workspace_bytes(B, K, SH2, D)
 """
@@ -62,6 +63,8 @@ _SIGNATURES = {
     "mamba2_scan_strerror": (ctypes.c_char_p, [_c_int]),
     "mamba2_scan_fwd_plan": (_c_int, [_c_int] * 4 + [_c_vp, _c_int]),
     "mamba2_scan_bwd_noalloc": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 8),
+    "mamba2_scan_bwd_full": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 10 + [_c_size, _c_vp]),
+    "mamba2_scan_bwd_full_bf16": (_c_int, [_c_int] * 4 + [_c_vp] * 3 + [_c_size] + [_c_vp] * 10 + [_c_size, _c_vp]),
 }
 
 
@@ -264,6 +267,44 @@ def bwd(h_history, h_s2, saved, d_context, *, workspace=None, out=None, debug=Fa
     res = dict(out)
     if debug:
         res.update(d_a=d_a, d_b=d_b, d_c=d_c)
+    return res
+
+
+def bwd_full(h_history, h_s2, saved, d_context, W_A, W_B, W_C, *, workspace=None, out=None,
+             want=("h_history", "h_s2"), stream=None):
+    """Backward with the input gradients (mamba2_scan_bwd_full).
+
+    Returns dict with dW_A, dW_B, dW_C [SH2, D], d_h_history [B, K, SH2] and
+    d_h_s2 [B, SH2]; an input gradient not named in `want` (and not passed in
+    `out`) comes back as None.
+    """
+    torch = _torch()
+    B, K, SH2, D, dev = _bwd_args(h_history, h_s2, saved, d_context)
+    for name, w in (("W_A", W_A), ("W_B", W_B), ("W_C", W_C)):
+        _check(w, name, (SH2, D), dev)
+    if workspace is None:
+        workspace = alloc_workspace(B, K, SH2, D, dev)
+    _check(workspace, "workspace", None, dev)
+    res = dict(out or {})
+    for n in ("dW_A", "dW_B", "dW_C"):
+        if res.get(n) is None:
+            res[n] = torch.empty((SH2, D), dtype=torch.float32, device=dev)
+        _check(res[n], n, (SH2, D), dev)
+    shapes = {"d_h_history": (B, K, SH2), "d_h_s2": (B, SH2)}
+    for n, shape in shapes.items():
+        if res.get(n) is None and n[2:] in want:
+            res[n] = torch.empty(shape, dtype=torch.float32, device=dev)
+        if res.get(n) is not None:
+            _check(res[n], n, shape, dev)
+        else:
+            res[n] = None
+    fn, name = ((lib().mamba2_scan_bwd_full_bf16, "mamba2_scan_bwd_full_bf16") if _is_bf16(h_history.dtype)
+                else (lib().mamba2_scan_bwd_full, "mamba2_scan_bwd_full"))
+    st = fn(B, K, SH2, D, _ptr(h_history), _ptr(h_s2), _ptr(saved), saved.numel() * 4, _ptr(d_context),
+            _ptr(W_A), _ptr(W_B), _ptr(W_C), _ptr(res["dW_A"]), _ptr(res["dW_B"]), _ptr(res["dW_C"]),
+            _ptr(res["d_h_history"]), _ptr(res["d_h_s2"]), _ptr(workspace), workspace.numel() * 4,
+            _stream(stream, dev))
+    _raise(st, name)
     return res
 
 

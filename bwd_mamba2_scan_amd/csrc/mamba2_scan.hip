@@ -127,6 +127,21 @@ __device__ __forceinline__ void split3_pk(float a, float b, unsigned& h, unsigne
   const float sa = ra - __uint_as_float(m << 16), sb = rb - __uint_as_float(m & 0xffff0000u);
   l = pk_bf16(sa, sb);
 }
+// Eight floats split exactly into three bf16 terms, as MFMA operands.
+__device__ __forceinline__ void split3_v8(const float (&v)[8], v8bf (&t)[3]) {
+  v4u w[3];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    unsigned h, mm, l;
+    split3_pk(v[2 * k], v[2 * k + 1], h, mm, l);
+    w[0][k] = h;
+    w[1][k] = mm;
+    w[2][k] = l;
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) t[k] = __builtin_bit_cast(v8bf, w[k]);
+}
+
 __device__ __forceinline__ void ld8_bf16(const bf16_t* p, v4f& lo, v4f& hi) {
   const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
   lo[0] = __uint_as_float(w[0] << 16);
@@ -1036,10 +1051,12 @@ __device__ __forceinline__ void bf16_tiles(const BwdUnit& U, v4bf (&a)[4]) {
   }
 }
 
+// dv (when the caller keeps it): the unit's d values as this lane holds
+// them, samples 4kg..4kg+3 of state n: [0] d_a or d_c, [1] d_b.
 template <bool DBG, bool ROUNDS, bool BF, class Ctx>
 __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const Ctx& c, v4f (&acc)[4][3],
                                             float* __restrict__ d_a_out, float* __restrict__ d_b_out,
-                                            float* __restrict__ d_c_out, bool write_dbg) {
+                                            float* __restrict__ d_c_out, bool write_dbg, float (&dv)[2][4]) {
   const BwdUnit& q = U;
   const int sbase = q.blk * kBlock + 4 * c.kg;
   if constexpr (BF) {
@@ -1059,6 +1076,11 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
           if (d_b_out) d_b_out[((size_t)s * c.K + q.t) * c.D + c.state] = db[i];
         }
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dv[0][i] = da[i];
+        dv[1][i] = db[i];
+      }
       v4bf ta[3], tb[3];
       bf16_split3(da, ta);
       bf16_split3(db, tb);
@@ -1077,6 +1099,8 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
         dd[i] = (ok ? U.dc[i] : 0.f) * U.al[i];
         if (DBG && write_dbg && ok && d_c_out) d_c_out[(size_t)(sbase + i) * c.D + c.state] = dd[i];
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dv[0][i] = dd[i];
       v4bf td[3];
       bf16_split3(dd, td);
 #pragma unroll
@@ -1094,6 +1118,8 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
       const float dc = ok ? (ROUNDS ? U.dc[i] * U.sr[i] : U.dc[i]) : 0.f;
       const float da = dc * U.al[i];
       const float db = dc * U.be[i];
+      dv[0][i] = da;
+      dv[1][i] = db;
       if (DBG && write_dbg && ok) {
         const int s = sbase + i;
         if (d_a_out) d_a_out[((size_t)s * c.K + q.t) * c.D + c.state] = da;
@@ -1110,6 +1136,7 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
     for (int i = 0; i < 4; ++i) {
       const bool ok = live && 4 * c.kg + i < q.nvalid;
       const float dcc = (ok ? U.dc[i] : 0.f) * U.al[i];
+      dv[0][i] = dcc;
       if (DBG && write_dbg && ok && d_c_out) d_c_out[(size_t)(sbase + i) * c.D + c.state] = dcc;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) acc[qq][2] = mfma16x16x4(U.h[i][qq], dcc, acc[qq][2]);
@@ -1117,14 +1144,97 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
   }
 }
 
-template <class T, bool DBG, bool ROUNDS>
-__global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
+// Input gradients inside the backward (STATE_D = 16: the work-group's state
+// group is every state).  A unit's d_h tile -- its 16 samples at this column
+// block's 64 features -- is
+//   d_h_history[b][t][j] = sum_s d_a[b,t,s] W_A[j][s] + d_b[b,t,s] W_B[j][s]
+// (or d_h_s2[b][j] = sum_s d_c[b,s] W_C[j][s] for the readout), the chain
+// rule through the projections.  The unit's d values go through the wave's
+// LDS tile from the backward's layout (lane (kg, n): samples 4kg..4kg+3 of
+// state n) to the input-gradient kernel's (lane (kg, n): sample n, states
+// 4kg..4kg+3), and then take exactly that kernel's MFMA sequence (M = 16
+// features x 4 tiles, N = the 16 samples, K = the states, W from LDS), so
+// d_h has the same bits as mamba2_scan_bwd_input.  Results leave through the
+// same tile as 256-byte row pieces; a descriptor of the unit's valid rows
+// drops the rest (and every store of a unit past the slice's last one).
+constexpr int kFusedDRow = 20;             // padded row of the d transpose
+constexpr int kFusedRow = kColBlock + 4;   // padded row of the output transpose
+constexpr int kFusedTile = kBlock * kFusedRow;  // floats per wave (the d transpose takes 32 * 20 of them)
+// staged weights: per 16-feature tile jt, W_A|W_B (kappa = 0..31) and W_C
+// (kappa = 0..15, zero above) as three bf16 terms in the
+// v_mfma_f32_16x16x32_bf16 A-operand layout, [W_AB | W_C][jt][term][lane]
+constexpr int kFusedW = 2 * 4 * 3 * 64 * 4;   // floats (16-byte entries)
+__device__ __forceinline__ void din_fused(const float (&dv)[2][4], bool readout, bool live, int blk, int t,
+                                          int B, int K, int SH2, int jb, int kg, int n, int lane,
+                                          float* __restrict__ tile, const float* __restrict__ sW,
+                                          float* __restrict__ dH, float* __restrict__ dhs2) {
+  // (1) the transpose: row kappa = state (d_b 16 rows further), column = sample
+  *reinterpret_cast<v4f*>(&tile[n * kFusedDRow + 4 * kg]) = v4f{dv[0][0], dv[0][1], dv[0][2], dv[0][3]};
+  *reinterpret_cast<v4f*>(&tile[(kGroup + n) * kFusedDRow + 4 * kg]) = v4f{dv[1][0], dv[1][1], dv[1][2], dv[1][3]};
+  __builtin_amdgcn_wave_barrier();
+  // B operand, lane (kg, n): sample n at kappa = 8kg .. 8kg+7 (the readout:
+  // d_c below 16, zero above), split exactly into three bf16 terms
+  float d8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = tile[(8 * kg + e) * kFusedDRow + n];
+    d8[e] = (readout && kg >= 2) ? 0.f : x;
+  }
+  __builtin_amdgcn_wave_barrier();
+  v8bf dt[3];
+  split3_v8(d8, dt);
+  // (2) per 16-feature tile jt: the six term products whose term indices
+  // sum to at most 2 (the three dropped are below 2^-23 of the product
+  // together), the result parked in the tile; (3) out through the tile:
+  // lane (kg, n) then stores features 4n..4n+3 of samples 4i + kg
+  const v4u* sw = reinterpret_cast<const v4u*>(sW) + (readout ? 4 * 3 * 64 : 0);
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tw = 2; tw >= 0; --tw) {
+      const v8bf w = __builtin_bit_cast(v8bf, sw[(jt * 3 + tw) * 64 + lane]);
+#pragma unroll
+      for (int td = 2 - tw; td >= 0; --td) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, dt[td], acc, 0, 0, 0);
+    }
+    *reinterpret_cast<v4f*>(&tile[n * kFusedRow + jt * 16 + 4 * kg]) = acc;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int nvalid = min(kBlock, B - blk * kBlock);
+  float* out = readout ? dhs2 : dH;
+  const size_t row_stride = readout ? (size_t)SH2 : (size_t)K * SH2;  // floats between samples
+  float* base = out == nullptr ? nullptr
+                               : out + (size_t)blk * kBlock * row_stride + (readout ? 0 : (size_t)t * SH2) +
+                                     jb * kColBlock;
+  const unsigned bytes = (out == nullptr || !live)
+                             ? 0u
+                             : (unsigned)(((size_t)(nvalid - 1) * row_stride + kColBlock) * sizeof(float));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v4f v = *reinterpret_cast<const v4f*>(&tile[(4 * i + kg) * kFusedRow + 4 * n]);
+    const unsigned off = (unsigned)(((size_t)(4 * i + kg) * row_stride + 4 * n) * sizeof(float));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rs, off, 0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// DIN (STATE_D = 16 only): also the input gradients d_h_history, d_h_s2 of
+// each unit, from the same d values (see din_fused), with W_A, W_B, W_C of
+// the column block staged in LDS.  The per-wave tiles and the staged W share
+// the LDS of the final slice sum.
+// NW waves per work-group: kBwdWaves, or 8 for the fp32 DIN form, which
+// needs more than the 168 registers that three waves per SIMD leave.
+template <class T, bool DBG, bool ROUNDS, bool DIN = false, int NW = kBwdWaves>
+__global__ __launch_bounds__(NW * 64) void bwd_partials_kernel(
     int B, int K, int SH2, int NG, int NB, int P, int UPW,
     const T* __restrict__ H, const T* __restrict__ hs2,
     const float* __restrict__ saved, const float* __restrict__ dctx,
     float* __restrict__ d_a_out, float* __restrict__ d_b_out, float* __restrict__ d_c_out,
-    float* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) float sRed[kBwdWaves][3 * kColBlock * kGroup];
+    float* __restrict__ ws, const float* __restrict__ WA, const float* __restrict__ WB,
+    const float* __restrict__ WC, float* __restrict__ dH, float* __restrict__ dhs2) {
+  __shared__ __attribute__((aligned(16))) float sRed[NW][3 * kColBlock * kGroup];
+  static_assert(NW * kFusedTile + kFusedW <= NW * 3 * kColBlock * kGroup, "fused tiles fit");
 
   const int NJB = SH2 / kColBlock;
   const int V = NJB * NG;
@@ -1170,7 +1280,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
 #pragma unroll
     for (int pl = 0; pl < 3; ++pl) acc[q][pl] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int S = kBwdWaves;
+  constexpr int S = NW;
   // Two-unit ring.  Requests are unconditional: past the last unit a wave
   // re-loads the last unit (unused), so the compiler's waits stay exact.
   // Both halves of an iteration always run: a unit past the last one (u >= n)
@@ -1180,14 +1290,54 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   BwdUnit R0, R1;
   int u = wave;
   bwd_load<ROUNDS>(R0, min(u, n - 1), c, lane);
+  float* sW = &sRed[0][0] + NW * kFusedTile;         // DIN: staged weights
+  float* tile = &sRed[0][0] + wave * kFusedTile;     // DIN: this wave's tile
+  if constexpr (DIN) {
+    // W of this column block as v_mfma_f32_16x16x32_bf16 A operands, three
+    // exact bf16 terms each: entry (jt, lane (kg, m)) holds row jb*64 +
+    // jt*16 + m at kappa = 8kg .. 8kg+7, W_A below 16 and W_B above for the
+    // steps, W_C below 16 and zeros above for the readout
+    for (int e = tid; e < 2 * 4 * 64; e += NW * 64) {
+      const bool ro = e >= 4 * 64;
+      const int l = e & 63, jt = (e >> 6) & 3, kgw = l >> 4;
+      const float* row = (ro ? WC : (kgw < 2 ? WA : WB)) + (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * kGroup +
+                         8 * (kgw & 1);
+      const v4f a = ld4(row), b = ld4(row + 4);
+      const bool zero = ro && kgw >= 2;
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[k] = zero ? 0.f : a[k];
+        v[4 + k] = zero ? 0.f : b[k];
+      }
+      v8bf tw[3];
+      split3_v8(v, tw);
+      v4u* dst = reinterpret_cast<v4u*>(sW) + (ro ? 4 * 3 * 64 : 0);
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm) dst[(jt * 3 + tm) * 64 + l] = __builtin_bit_cast(v4u, tw[tm]);
+    }
+    __syncthreads();
+  }
   for (; u < n; u += 2 * S) {
+    float dv[2][4];
     bwd_load<ROUNDS>(R1, min(u + S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
-    bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg, dv);
+    if constexpr (DIN) {
+      din_fused(dv, R0.t == K, u < n, R0.blk, R0.t, B, K, SH2, jb, kg, m, lane, tile, sW, dH, dhs2);
+      __builtin_amdgcn_sched_barrier(0);  // the next unit's loads stay after (registers)
+    }
     bwd_load<ROUNDS>(R0, min(u + 2 * S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
-    bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg, dv);
+    if constexpr (DIN) {
+      din_fused(dv, R1.t == K, u + S < n, R1.blk, R1.t, B, K, SH2, jb, kg, m, lane, tile, sW, dH, dhs2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  // DIN: every wave is done with its tile and the staged W before sRed
+  // (the same LDS) takes the partial sums
+  if constexpr (DIN) __syncthreads();
 
   // Result lane (g = kg, n = m), element r of tile q: feature row
   // jl = 16*g + 4*r + q of the column block, state n.  Slices keep that
@@ -1205,10 +1355,10 @@ __global__ __launch_bounds__(kBwdWaves * 64) void bwd_partials_kernel(
   // remain to be written back before the reduce can start.
   float* out = ws + ((size_t)sg * P + p) * ((size_t)SH2 * 3 * kGroup) + (size_t)jb * (3 * kColBlock * kGroup);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(out, 3 * kColBlock * kGroup * sizeof(float));
-  for (int e = 4 * tid; e < 3 * kColBlock * kGroup; e += 4 * kBwdWaves * 64) {
+  for (int e = 4 * tid; e < 3 * kColBlock * kGroup; e += 4 * NW * 64) {
     v4f s = *reinterpret_cast<const v4f*>(&sRed[0][e]);
 #pragma unroll
-    for (int w = 1; w < kBwdWaves; ++w) s += *reinterpret_cast<const v4f*>(&sRed[w][e]);
+    for (int w = 1; w < NW; ++w) s += *reinterpret_cast<const v4f*>(&sRed[w][e]);
     st4_through(rs, (unsigned)(e * sizeof(float)), s);
   }
 }
@@ -1544,20 +1694,6 @@ struct DinWs {
   }
 };
 
-// Eight floats split exactly into three bf16 terms, as MFMA operands.
-__device__ __forceinline__ void split3_v8(const float (&v)[8], v8bf (&t)[3]) {
-  v4u w[3];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    unsigned h, mm, l;
-    split3_pk(v[2 * k], v[2 * k + 1], h, mm, l);
-    w[0][k] = h;
-    w[1][k] = mm;
-    w[2][k] = l;
-  }
-#pragma unroll
-  for (int k = 0; k < 3; ++k) t[k] = __builtin_bit_cast(v8bf, w[k]);
-}
 
 template <int NGT, bool ROUNDS, class WOps>
 __device__ __forceinline__ void din_compute(const DinUnit<NGT>& U, int u, const DinCtx& c, int SH2, int jb, int kg,
@@ -1960,16 +2096,24 @@ int check_reduce(const Plan& pl, const void* ws, size_t ws_bytes, const float* d
   return MAMBA2_SCAN_OK;
 }
 
+// din: the input gradients in the same launch (STATE_D = 16 only; no debug
+// outputs), from W_A/W_B/W_C into dH / dhs2.
 template <class T>
 void launch_partials(const Plan& pl, const T* H, const T* hs2, const void* saved, const float* dctx,
-                     float* da, float* db, float* dc, void* ws, hipStream_t st) {
+                     float* da, float* db, float* dc, void* ws, hipStream_t st, bool din = false,
+                     const float* WA = nullptr, const float* WB = nullptr, const float* WC = nullptr,
+                     float* dH = nullptr, float* dhs2 = nullptr) {
   const int grid = 8 * pl.V * ((pl.P + 7) / 8);
   const bool dbg = da || db || dc, rounds = pl.K > kChunk;
-  auto kern = dbg ? (rounds ? bwd_partials_kernel<T, true, true> : bwd_partials_kernel<T, true, false>)
-                  : (rounds ? bwd_partials_kernel<T, false, true> : bwd_partials_kernel<T, false, false>);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBwdWaves * 64), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
+  constexpr int NWD = sizeof(T) == 4 ? 8 : kBwdWaves;  // waves of the DIN form
+  auto kern = din ? (rounds ? bwd_partials_kernel<T, false, true, true, NWD>
+                            : bwd_partials_kernel<T, false, false, true, NWD>)
+              : dbg ? (rounds ? bwd_partials_kernel<T, true, true> : bwd_partials_kernel<T, true, false>)
+                    : (rounds ? bwd_partials_kernel<T, false, true> : bwd_partials_kernel<T, false, false>);
+  const int threads = (din ? NWD : kBwdWaves) * 64;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
                      pl.NB, pl.P, pl.UPW, H, hs2, static_cast<const float*>(saved), dctx, da, db, dc,
-                     static_cast<float*>(ws));
+                     static_cast<float*>(ws), WA, WB, WC, dH, dhs2);
 }
 
 void launch_reduce(const Plan& pl, const void* ws, float* dWA, float* dWB, float* dWC, hipStream_t st,
@@ -2324,6 +2468,67 @@ int mamba2_scan_fwd_plan(int B, int K, int SH2, int STATE_D, mamba2_scan_launch*
   const int n = fwd_plan(pl, ls);
   for (int i = 0; i < n && i < max_launches; ++i) launches[i] = ls[i];
   return n;
+}
+
+}  // extern "C"
+
+namespace {
+// The backward with the input gradients: one pass over the history when
+// STATE_D = 16, else the weight-gradient backward then the input-gradient
+// kernel (the same results as the two separate calls).
+template <class T>
+int run_bwd_full(int B, int K, int SH2, int STATE_D, const T* H, const T* hs2, const void* saved,
+                 size_t saved_bytes, const float* dctx, const float* WA, const float* WB, const float* WC,
+                 float* dWA, float* dWB, float* dWC, float* dH, float* dhs2, void* ws, size_t ws_bytes,
+                 void* stream) {
+  Plan pl;
+  int st = make_plan(B, K, SH2, STATE_D, &pl);
+  if (st != MAMBA2_SCAN_OK) return st;
+  // a 16-sample block's rows must span less than 4 GiB (32-bit store offsets)
+  if ((long long)K * SH2 > kDinMaxRowFloats) return MAMBA2_SCAN_EUNSUPPORTED;
+  st = check_bwd_common(pl, H, hs2, saved, saved_bytes, dctx, nullptr, nullptr, nullptr, ws, ws_bytes);
+  if (st != MAMBA2_SCAN_OK) return st;
+  st = check_reduce(pl, ws, ws_bytes, dWA, dWB, dWC);
+  if (st != MAMBA2_SCAN_OK) return st;
+  if (!WA || !WB || !WC || (!dH && !dhs2)) return MAMBA2_SCAN_ENULL;
+  if (!aligned16(WA) || !aligned16(WB) || !aligned16(WC) || !aligned16(dH) || !aligned16(dhs2))
+    return MAMBA2_SCAN_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fused = pl.NG == 1;
+  launch_partials(pl, H, hs2, saved, dctx, nullptr, nullptr, nullptr, ws, s, fused, WA, WB, WC, dH, dhs2);
+  st = launch_status();
+  if (st != MAMBA2_SCAN_OK) return st;
+  launch_reduce(pl, ws, dWA, dWB, dWC, s);
+  st = launch_status();
+  if (st != MAMBA2_SCAN_OK || fused) return st;
+  const float* sv = static_cast<const float*>(saved);
+  switch (pl.NG) {
+    case 2: launch_dinput<2>(pl, WA, WB, WC, sv, dctx, dH, dhs2, s); break;
+    case 4: launch_dinput<4>(pl, WA, WB, WC, sv, dctx, dH, dhs2, s); break;
+    default: return MAMBA2_SCAN_EUNSUPPORTED;
+  }
+  return launch_status();
+}
+}  // namespace
+
+extern "C" {
+
+int mamba2_scan_bwd_full(int B, int K, int SH2, int STATE_D, const float* h_history, const float* h_s2,
+                         const void* saved, size_t saved_bytes, const float* d_context, const float* W_A,
+                         const float* W_B, const float* W_C, float* dW_A, float* dW_B, float* dW_C,
+                         float* d_h_history, float* d_h_s2, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_bwd_full(B, K, SH2, STATE_D, h_history, h_s2, saved, saved_bytes, d_context, W_A, W_B, W_C, dW_A,
+                      dW_B, dW_C, d_h_history, d_h_s2, workspace, workspace_bytes, stream);
+}
+
+int mamba2_scan_bwd_full_bf16(int B, int K, int SH2, int STATE_D, const void* h_history, const void* h_s2,
+                              const void* saved, size_t saved_bytes, const float* d_context, const float* W_A,
+                              const float* W_B, const float* W_C, float* dW_A, float* dW_B, float* dW_C,
+                              float* d_h_history, float* d_h_s2, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return run_bwd_full(B, K, SH2, STATE_D, static_cast<const bf16_t*>(h_history), static_cast<const bf16_t*>(h_s2),
+                      saved, saved_bytes, d_context, W_A, W_B, W_C, dW_A, dW_B, dW_C, d_h_history, d_h_s2, workspace,
+                      workspace_bytes, stream);
 }
 
 const char* mamba2_scan_strerror(int status) {

@@ -185,6 +185,36 @@ int mamba2_scan_bwd_input(int B, int K, int SH2, int STATE_D,
                           void* stream);
 
 /*
+ * The backward and the input gradients together: dW_A, dW_B, dW_C as
+ * mamba2_scan_bwd and d_h_history [B][K][SH2], d_h_s2 [B][SH2] as
+ * mamba2_scan_bwd_input.  Training the trunk through the scan needs both.
+ * Every output is bitwise reproducible and agrees with those two calls to
+ * fp32 rounding.  The one-pass form contracts with bf16 MFMAs on exact
+ * three-term splits of both operands, as the forward does.  With fp32 trunk
+ * inputs it sums its split-K partials over 8 waves per work-group instead
+ * of 12, another fixed order.  When STATE_D = 16 it makes one
+ * pass over the history instead of two: the backward's work-groups, which
+ * form each 16-sample block's d_a, d_b (per step) and d_c (readout) for one
+ * 64-feature column block, also multiply them into W_A, W_B, W_C for that
+ * block's 64 input-gradient features (the chain rule through the plan's
+ * Task 1 step 2 projections).  Other widths run the two calls in sequence.
+ *   W_A, W_B, W_C   the forward's weights [SH2][STATE_D], 16-byte aligned (in)
+ *   d_h_history, d_h_s2  (out, overwritten, 16-byte aligned); either may be
+ *                   NULL to skip it, not both
+ * The other arguments are as for mamba2_scan_bwd (no debug outputs).
+ * Supports K * SH2 <= 2^26 (MAMBA2_SCAN_EUNSUPPORTED beyond).
+ */
+int mamba2_scan_bwd_full(int B, int K, int SH2, int STATE_D,
+                         const float* h_history, const float* h_s2,
+                         const void* saved, size_t saved_bytes,
+                         const float* d_context,
+                         const float* W_A, const float* W_B, const float* W_C,
+                         float* dW_A, float* dW_B, float* dW_C,
+                         float* d_h_history, float* d_h_s2,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * The step after the path, with the stability multiplier (implementation
  * plan, Task 1 step 3).  As mamba2_scan_fwd, except:
  *   - the gate is m * sigmoid(a) with m = *stability (a device scalar, such
@@ -264,6 +294,15 @@ int mamba2_scan_bwd_partials_bf16(int B, int K, int SH2, int STATE_D,
                                   float* d_a, float* d_b, float* d_c,
                                   void* workspace, size_t workspace_bytes,
                                   void* stream);
+int mamba2_scan_bwd_full_bf16(int B, int K, int SH2, int STATE_D,
+                              const void* h_history, const void* h_s2,
+                              const void* saved, size_t saved_bytes,
+                              const float* d_context,
+                              const float* W_A, const float* W_B, const float* W_C,
+                              float* dW_A, float* dW_B, float* dW_C,
+                              float* d_h_history, float* d_h_s2,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
 int mamba2_scan_bwd_bf16(int B, int K, int SH2, int STATE_D,
                          const void* h_history, const void* h_s2,
                          const void* saved, size_t saved_bytes,

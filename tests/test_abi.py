@@ -25,6 +25,7 @@ def test_exports_every_header_symbol(L):
         "mamba2_scan_fwd_blend", "mamba2_scan_bwd_blend_workspace_bytes", "mamba2_scan_bwd_blend",
         "mamba2_scan_fwd_bf16", "mamba2_scan_bwd_bf16", "mamba2_scan_bwd_partials_bf16",
         "mamba2_scan_strerror", "mamba2_scan_fwd_plan", "mamba2_scan_bwd_noalloc",
+        "mamba2_scan_bwd_full", "mamba2_scan_bwd_full_bf16",
     }
     for n in names:
         assert hasattr(L, n), n
@@ -228,3 +229,26 @@ def test_noalloc_argument_checks(L):
     assert call(da=ctypes.c_void_p(0x20001)) == m2.EALIGN
     assert m2.strerror(m2.ESCRATCH) != "unknown status"
 
+
+
+@pytest.mark.parametrize("fn", ["mamba2_scan_bwd_full", "mamba2_scan_bwd_full_bf16"])
+def test_bwd_full_argument_checks(L, fn):
+    dims = (100, 5, 192, 16)
+    sv, ws = m2.saved_bytes(*dims), m2.workspace_bytes(*dims)
+    g = ctypes.c_void_p(0x20000)
+    f = getattr(L, fn)
+
+    def call(*, dims=dims, h=g, hs=g, saved=g, svb=sv, dctx=g, wa=g, wb=g, wc=g, dwa=g, dwb=g, dwc=g, dh=g, dhs=g,
+             w=g, wsb=ws):
+        return f(*dims, h, hs, saved, svb, dctx, wa, wb, wc, dwa, dwb, dwc, dh, dhs, w, wsb, None)
+
+    assert call(dims=(0, 5, 192, 16)) == m2.EBADDIM
+    assert call(dims=(100, 5, 100, 16)) == m2.EUNSUPPORTED
+    assert call(dims=(100, 2 ** 18, 512, 16)) == m2.EUNSUPPORTED  # K * SH2 > 2^26
+    for k in ("h", "hs", "saved", "dctx", "wa", "wb", "wc", "dwa", "dwb", "dwc", "w"):
+        assert call(**{k: None}) == m2.ENULL, k
+    assert call(dh=None, dhs=None) == m2.ENULL
+    assert call(svb=sv - 4) == m2.ESIZE
+    assert call(wsb=ws - 4) == m2.ESIZE
+    for k in ("wa", "dh", "dhs"):
+        assert call(**{k: ctypes.c_void_p(0x20004)}) == m2.EALIGN, k
