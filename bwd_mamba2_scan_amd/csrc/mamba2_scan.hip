@@ -1580,6 +1580,13 @@ __global__ __launch_bounds__(kBlendWaves * 64) void blend_bwd_kernel(
 // descriptor rather than by a branch, so the compiler's memory-counter waits
 // stay exact and the next unit's requests stay in flight.
 constexpr int kDinWaves = 4;
+// One state group: each wave issues the loads of all its units (at most
+// kDinBatch) before its first store.  A CU's memory pipe completes requests
+// in issue order, so a unit's loads issued after earlier units' stores waited
+// for those stores (4 KiB per unit) to drain; loaded up front, a unit's data
+// is there when the wave reaches it (24.5 -> 21.2 us at 8192 samples).
+constexpr int kDinBatch = 6;
+constexpr long long kDinMaxWGs = 4096;  // one state group: a longer slice beyond this many work-groups
 constexpr int kDinTargetWGs = 4096 / kDinWaves;      // 16 resident waves per CU
 constexpr int kDinTargetWGsRounds = 2 * kDinTargetWGs;  // multi-round histories: shorter slices balance better
 constexpr int kDinRow = kColBlock + 4;               // padded LDS row of the output transpose
@@ -1869,10 +1876,12 @@ __global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
   const int kg = lane >> 4;
   const int n = lane & 15;
 
-  // The first unit's operands go out before the weights.
   constexpr int S = kDinWaves;
+  constexpr bool BATCH = NGT == 1;  // every unit loaded up front (UPW <= kDinBatch * S)
   DinUnit<NGT> R0, R1;
-  din_load<NGT, ROUNDS>(R0, min(wave, n_units - 1), c, lane);
+  DinUnit<NGT> UB[BATCH ? kDinBatch : 1];
+  // The ring: the first unit's operands go out before the weights.
+  if constexpr (!BATCH) din_load<NGT, ROUNDS>(R0, min(wave, n_units - 1), c, lane);
 
   if constexpr (SPLIT) {
     // lane l of (tile jt, chunk h): feature row jb*64 + jt*16 + l%16, the
@@ -1905,6 +1914,29 @@ __global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
 #pragma unroll
       for (int tm = 0; tm < 3; ++tm) dst[((jt * nc + h) * 3 + tm) * nl + l] = __builtin_bit_cast(v4u, tw[tm]);
     }
+  } else if constexpr (BATCH) {
+    // The weights' loads go out first (they return first), then every
+    // unit's (a slot past the last unit re-loads it, unused), then the
+    // weights go into LDS.
+    static_assert(4 * 2 * NGT * 64 == 2 * kDinWaves * 64 && 4 * NGT * 64 == kDinWaves * 64, "one W_C, two W_A|W_B float4s per thread");
+    v4f wab[2], wcv;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + i * kDinWaves * 64;
+      const int l = e & 63, qq = (e >> 6) % (2 * NGT), jt = (e >> 6) / (2 * NGT);
+      const size_t row = (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * D + 4 * (l >> 4);
+      wab[i] = ld4(din_w_src(WA, WB, NGT, qq) + row + 16 * (qq % NGT));
+    }
+    {
+      const int l = tid & 63, jt = tid >> 6;
+      const size_t row = (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * D + 4 * (l >> 4);
+      wcv = ld4(WC + row);
+    }
+#pragma unroll
+    for (int k = 0; k < kDinBatch; ++k) din_load<NGT, ROUNDS>(UB[k], min(wave + k * S, n_units - 1), c, lane);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<v4f*>(&sWab[(tid + i * kDinWaves * 64) * 4]) = wab[i];
+    *reinterpret_cast<v4f*>(&sWc[tid * 4]) = wcv;
   } else {
     for (int e = tid; e < 4 * 2 * NGT * 64; e += kDinWaves * 64) {
       const int l = e & 63, qq = (e >> 6) % (2 * NGT), jt = (e >> 6) / (2 * NGT);
@@ -1928,6 +1960,25 @@ __global__ __launch_bounds__(kDinWaves * 64) void dinput_kernel(
   W.lane = lane;
   __syncthreads();
 
+  if constexpr (BATCH) {
+#pragma unroll
+    for (int k = 0; k < kDinBatch; ++k) {
+      const int u = wave + k * S;
+      if (u < n_units) din_compute<NGT, ROUNDS>(UB[k], u, c, SH2, jb, kg, n, W, sTile[wave], lane, dH, dhs2);
+    }
+    // further batches: slices longer than one batch per wave (large inputs,
+    // whose grid is held to kDinMaxWGs)
+    for (int b0 = wave + kDinBatch * S; b0 < n_units; b0 += kDinBatch * S) {
+#pragma unroll
+      for (int k = 0; k < kDinBatch; ++k) din_load<NGT, ROUNDS>(UB[k], min(b0 + k * S, n_units - 1), c, lane);
+#pragma unroll
+      for (int k = 0; k < kDinBatch; ++k) {
+        const int u = b0 + k * S;
+        if (u < n_units) din_compute<NGT, ROUNDS>(UB[k], u, c, SH2, jb, kg, n, W, sTile[wave], lane, dH, dhs2);
+      }
+    }
+    return;
+  }
   // Two-unit ring; a request past the last unit re-loads the last unit (unused).
   for (int u = wave; u < n_units; u += 2 * S) {
     din_load<NGT, ROUNDS>(R1, min(u + S, n_units - 1), c, lane);
@@ -2177,13 +2228,20 @@ size_t blend_ws_bytes(const Plan& pl) {
 // into slices so that about kDinTargetWGs work-groups run (twice as many when
 // K spans several rounds: K = 64 and long_few ran 3 % faster, the pages'
 // shape 5 % slower), at least one unit per wave, whatever the mix of samples
-// and history length.
+// and history length.  One state group: at most one batch of units per wave
+// (more work-groups, up to kDinMaxWGs).
 int dinput_upw(const Plan& pl) {
   const long long units = (long long)pl.NB * (pl.K + 1);
   const int target = pl.K > kChunk ? kDinTargetWGsRounds : kDinTargetWGs;
   const long long slices = (target + pl.NJB - 1) / pl.NJB;
   long long upw = (units + slices - 1) / slices;
   if (upw < kDinWaves) upw = kDinWaves;
+  if (pl.NG == 1) {
+    // one batch per wave where at most kDinMaxWGs work-groups do it
+    const long long fit = (units * pl.NJB + kDinMaxWGs - 1) / kDinMaxWGs;
+    const long long cap = fit > kDinBatch * kDinWaves ? fit : kDinBatch * kDinWaves;
+    if (upw > cap) upw = cap;
+  }
   return (int)(upw > units ? units : upw);
 }
 
