@@ -63,8 +63,9 @@ def algorithmic_bytes(B, K, SH2, D, trunk_bytes=4):
         "fwd_kernel": fwd,
         "bwd_partials_kernel": H + hs2 + vec,
         "bwd_reduce_kernel": W,
-        # optional input gradients: read W and d_context, write d_h_history and d_h_s2
-        "dinput_kernel": W + vec + H + hs2,
+        # optional input gradients: read W and d_context, write d_h_history and
+        # d_h_s2 (fp32 whatever the trunk precision)
+        "dinput_kernel": W + vec + (B * K * SH2 + B * SH2) * f,
     }
     # the backward with the input gradients: its reads and dW writes, plus the
     # d_h_history and d_h_s2 writes (fp32 whatever the trunk precision)
