@@ -1158,8 +1158,13 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
 // same tile as 256-byte row pieces; a descriptor of the unit's valid rows
 // drops the rest (and every store of a unit past the slice's last one).
 constexpr int kFusedDRow = 20;             // padded row of the d transpose
+// Row r of the d transpose: each 8-row group 16 floats further on, so that
+// the column reads of lanes kg = 0, 1 (rows 8kg + e) fall in disjoint halves
+// of the 32 banks; the 16-byte row writes of 8 lanes stay distinct.
+__device__ __forceinline__ int fused_drow(int r) { return r * kFusedDRow + (r >> 3) * 16; }
 constexpr int kFusedRow = kColBlock + 4;   // padded row of the output transpose
-constexpr int kFusedTile = kBlock * kFusedRow;  // floats per wave (the d transpose takes 32 * 20 of them)
+constexpr int kFusedTile = kBlock * kFusedRow;  // floats per wave (the d transpose takes fused_drow(31) + 20 = 688)
+static_assert(31 * kFusedDRow + 3 * 16 + kFusedDRow <= kFusedTile, "the d transpose fits the tile");
 // staged weights: per 16-feature tile jt, W_A|W_B (kappa = 0..31) and W_C
 // (kappa = 0..15, zero above) as three bf16 terms in the
 // v_mfma_f32_16x16x32_bf16 A-operand layout, [W_AB | W_C][jt][term][lane]
@@ -1169,15 +1174,15 @@ __device__ __forceinline__ void din_fused(const float (&dv)[2][4], bool readout,
                                           float* __restrict__ tile, const float* __restrict__ sW,
                                           float* __restrict__ dH, float* __restrict__ dhs2) {
   // (1) the transpose: row kappa = state (d_b 16 rows further), column = sample
-  *reinterpret_cast<v4f*>(&tile[n * kFusedDRow + 4 * kg]) = v4f{dv[0][0], dv[0][1], dv[0][2], dv[0][3]};
-  *reinterpret_cast<v4f*>(&tile[(kGroup + n) * kFusedDRow + 4 * kg]) = v4f{dv[1][0], dv[1][1], dv[1][2], dv[1][3]};
+  *reinterpret_cast<v4f*>(&tile[fused_drow(n) + 4 * kg]) = v4f{dv[0][0], dv[0][1], dv[0][2], dv[0][3]};
+  *reinterpret_cast<v4f*>(&tile[fused_drow(kGroup + n) + 4 * kg]) = v4f{dv[1][0], dv[1][1], dv[1][2], dv[1][3]};
   __builtin_amdgcn_wave_barrier();
   // B operand, lane (kg, n): sample n at kappa = 8kg .. 8kg+7 (the readout:
   // d_c below 16, zero above), split exactly into three bf16 terms
   float d8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float x = tile[(8 * kg + e) * kFusedDRow + n];
+    const float x = tile[fused_drow(8 * kg + e) + n];
     d8[e] = (readout && kg >= 2) ? 0.f : x;
   }
   __builtin_amdgcn_wave_barrier();
