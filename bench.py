@@ -10,10 +10,14 @@ set s % R and the backward of set (s - R/2) % R, so between a set's forward
 and its backward R/2 other steps stream far more than the cache holds.
 The K timed steps are one captured HIP graph of exactly K steps (steps
 0..K-1 of the rotation), timed with HIP events on the stream it is
-replayed on and bracketed by device synchronisation, so the figure does not
-depend on K.  A graph's first replay costs more than later ones (about 3 us
-per step), so after the W warmup steps the timed graph is replayed once
-untimed; that replay's time is reported as first_replay_ms_per_step.
+replayed on and bracketed by device synchronisation.  Ahead of the first
+event the stream runs a short spin kernel (about 0.4 ms) while the host
+submits the graph, so the events bracket the K steps' kernels and not the
+host's graph-launch latency (about 60 us per replay, which at K = 20 read
+as 3 us per step); the wall-clock figure keeps both.  A graph's first
+replay costs more than later ones (about 3 us per step), so after the W
+warmup steps the timed graph is replayed once untimed; that replay's time
+is reported as first_replay_ms_per_step.
 
 Warm protocol (secondary): K steps of fwd then bwd of one set, back to back
 in one graph, so the backward may find the batch in the Infinity Cache.
@@ -44,6 +48,7 @@ MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
 SRC = os.path.join(ROOT, "bwd_mamba2_scan_amd", "csrc", "mamba2_scan.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pages_shape.json")
 MAX_STEPS = 2000  # steps of the one captured graph that is timed
+HOLD_CYCLES = 1_000_000  # GPU clock cycles of the spin ahead of a timed replay (~0.4 ms)
 BLEND_STABILITY = 0.95  # the blend measurement's gate multiplier
 
 
@@ -336,6 +341,7 @@ def main():
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             t0 = time.perf_counter()
+            torch.cuda._sleep(HOLD_CYCLES)  # the host submits the graph meanwhile
             e0.record(stream)
             g.replay()
             e1.record(stream)
@@ -357,6 +363,7 @@ def main():
         for _ in range(max(4, args.steps // R)):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(HOLD_CYCLES)
             e0.record(stream)
             cycle.replay()
             e1.record(stream)
@@ -567,7 +574,7 @@ def main():
             "workload": args.workload, "B": B, "K": K, "SH2": SH2, "STATE_D": D, "trunk": args.trunk,
             "protocol": f"cold: {R} rotating input sets, fwd(set s) + bwd(set s-{R // 2}) per step; "
                         f"the {args.steps} timed steps are one HIP graph, replayed once untimed, then timed "
-                        f"with HIP events",
+                        f"with HIP events after a ~0.4 ms GPU spin that covers the host's graph submission",
         },
         "hbm_roofline_frac": round(hbm_us / (ms_per_step * 1e3), 4),
         "roofline_frac_step": round(roofline_us / (ms_per_step * 1e3), 4),
