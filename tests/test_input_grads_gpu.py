@@ -65,6 +65,19 @@ def test_input_grads_long_few(B, K, SH2, D):
     assert_elementwise(dhs2.cpu().numpy(), ref.d_h_s2, "d_h_s2")
 
 
+def test_input_grads_several_batches():
+    """A slice longer than one batch of units per wave: 50 samples, K = 6144,
+    SH2 = 256 give 24,580 (block, step) units per column block, so the grid cap
+    makes slices of 25 units per 4-wave work-group and a wave's seventh unit
+    comes in a second, partial batch; every output against the oracle."""
+    B, K, SH2, D = 50, 6144, 256, 16
+    inputs = make_inputs(B, K, SH2, D, seed=23, gate_bias=2.0)
+    dH, dhs2, _ = gpu_input_grads(_to_dev(inputs), K)
+    ref = oracle_input_grads(inputs)
+    assert_elementwise(dH.cpu().numpy(), ref.d_h_history, "d_h_history")
+    assert_elementwise(dhs2.cpu().numpy(), ref.d_h_s2, "d_h_s2")
+
+
 @pytest.mark.parametrize("name", ["long_history", "wide_state", "long_few"])
 def test_input_grads_large_sampled(name):
     """Full-size launch; up to 512 samples (both ends, the middle, random) checked."""
