@@ -231,6 +231,26 @@ def test_noalloc_argument_checks(L):
 
 
 
+def test_noalloc_scratch_covers_every_shape():
+    """The allocation-free backward's 4 MiB buffer holds the split-K slices of
+    every supported shape: a sweep over sample counts, history lengths, trunk
+    widths and state widths never asks for more."""
+    limit = 4 << 20
+    worst = (0, None)
+    Bs = list(range(1, 65)) + [100, 255, 256, 257, 1000, 1024, 4096, 8192, 32768, 100000, 1 << 20]
+    Ks = [1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 32, 33, 64, 100, 1000, 2048, 8192, 65536]
+    for D in (16, 32, 64):
+        for SH2 in range(64, 513, 64):
+            for K in Ks:
+                for B in Bs:
+                    if m2.saved_bytes(B, K, SH2, D) == 0:
+                        continue  # beyond the supported sizes
+                    ws = m2.workspace_bytes(B, K, SH2, D)
+                    assert 0 < ws <= limit, (B, K, SH2, D, ws)
+                    worst = max(worst, (ws, (B, K, SH2, D)))
+    assert worst[0] > limit // 2, worst  # the sweep reaches the large-slice shapes
+
+
 @pytest.mark.parametrize("fn", ["mamba2_scan_bwd_full", "mamba2_scan_bwd_full_bf16"])
 def test_bwd_full_argument_checks(L, fn):
     dims = (100, 5, 192, 16)
