@@ -68,7 +68,6 @@ constexpr int kChunk = kFwdWaves;  // history steps projected per forward round
 // CU still runs sixteen forward waves; one otherwise (two work-groups per
 // CU, which measured faster there).
 __host__ __device__ constexpr int fwd_blocks(int nkc) { return nkc >= 20 ? 2 : 1; }
-__host__ __device__ constexpr int fwd_threads(int nkc) { return fwd_blocks(nkc) * kFwdWaves * 64; }
 constexpr int kFwdPrefetch = 4;    // fp32 history loads each forward wave keeps in flight
 constexpr int kCUs = 256;            // compute units of an MI355X
 constexpr int kFwdPairPrefetch = 4;  // bf16 history loads (64 features of 8 rows) each wave keeps in flight
@@ -1151,12 +1150,15 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
 // (or d_h_s2[b][j] = sum_s d_c[b,s] W_C[j][s] for the readout), the chain
 // rule through the projections.  The unit's d values go through the wave's
 // LDS tile from the backward's layout (lane (kg, n): samples 4kg..4kg+3 of
-// state n) to the input-gradient kernel's (lane (kg, n): sample n, states
-// 4kg..4kg+3), and then take exactly that kernel's MFMA sequence (M = 16
-// features x 4 tiles, N = the 16 samples, K = the states, W from LDS), so
-// d_h has the same bits as mamba2_scan_bwd_input.  Results leave through the
-// same tile as 256-byte row pieces; a descriptor of the unit's valid rows
-// drops the rest (and every store of a unit past the slice's last one).
+// state n) to the B-operand layout of v_mfma_f32_16x16x32_bf16 (lane
+// (kg, n): sample n, kappa = 8kg .. 8kg+7 of [d_a | d_b]), split exactly
+// into three bf16 terms; W comes from LDS as three terms as well, and the
+// six term products whose indices sum to at most 2 accumulate in fp32
+// (M = 16 features x 4 tiles, N = the 16 samples, K = the 32 states).  The
+// result agrees with mamba2_scan_bwd_input to fp32 rounding (that kernel
+// uses fp32 MFMAs at STATE_D = 16).  Results leave through the same tile as
+// 256-byte row pieces; a descriptor of the unit's valid rows drops the rest
+// (and every store of a unit past the slice's last one).
 constexpr int kFusedDRow = 20;             // padded row of the d transpose
 // Row r of the d transpose: each 8-row group 16 floats further on, so that
 // the column reads of lanes kg = 0, 1 (rows 8kg + e) fall in disjoint halves
@@ -1566,10 +1568,13 @@ __global__ __launch_bounds__(kBlendWaves * 64) void blend_bwd_kernel(
 //   grid = 8 * (SH2/64) * ceil(NSL / 8), 256 threads.  A unit is (sample
 //   block, step t) for t < K, or the readout (t = K), numbered block-major;
 //   work-group: a slice of UPW consecutive units (so few samples with a long
-//   history still spread over ~1024 work-groups) and one 64-feature column
+//   history still spread over ~1024 work-groups, up to kDinMaxWGs with one
+//   state group) and one 64-feature column
 //   block; the column blocks of a slice run on one XCD so they share the
-//   saved planes in L2.  Wave w takes units w, w+4, ... of its slice and
-//   requests the next unit's operands while it multiplies the current one.
+//   saved planes in L2.  Wave w takes units w, w+4, ... of its slice.  With
+//   one state group it loads all of them (up to kDinBatch) before its first
+//   store; otherwise it requests the next unit's operands while it
+//   multiplies the current one.
 // Operands: a unit's saved planes and the block's d_context arrive as whole
 // 1 KiB rows (one 16-byte load per lane each, four per unit at D = 16) and
 // pass through the wave's LDS tile into the MFMA layout.  The kernel writes
