@@ -987,7 +987,11 @@ struct BwdCtx {
 // the compiler's memory-counter waits stay exact, so the next unit's loads
 // (issued before this unit is consumed) stay in flight.  Rows of samples past
 // B (last block only) re-read a valid row; their d_context is masked to zero.
-template <bool ROUNDS, class T>
+// SHARE (several state groups): the work-groups of a slice's column block,
+// one per state group, read the same history tiles on one XCD, so those
+// loads go through L2 as ordinary loads; with one state group each tile is
+// read once and streams with the non-temporal hint.
+template <bool ROUNDS, bool SHARE, class T>
 __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, int lane) {
   // unit u of the work-group's slice: block and step (t == K: the readout)
   const int ug = c.u0 + u;
@@ -1014,9 +1018,9 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, 
     const bool ok = 4 * c.kg + i < q.nvalid;
     const T* hp = rows + (size_t)s0 * rstride + (ok ? hk : 0) + c.col;
     if constexpr (sizeof(T) == 2)
-      U.hr[i] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(hp));
+      U.hr[i] = SHARE ? *reinterpret_cast<const v2u*>(hp) : __builtin_nontemporal_load(reinterpret_cast<const v2u*>(hp));
     else
-      U.h[i] = ld4_in(hp);
+      U.h[i] = SHARE ? ld4(reinterpret_cast<const float*>(hp)) : ld4_in(hp);
     U.dc[i] = c.dctx[(size_t)s0 * c.D + (ok ? 4 * c.kg * c.D : 0) + c.state];
   }
 }
@@ -1232,7 +1236,7 @@ __device__ __forceinline__ void din_fused(const float (&dv)[2][4], bool readout,
 // the LDS of the final slice sum.
 // NW waves per work-group: kBwdWaves, or 8 for the fp32 DIN form, which
 // needs more than the 168 registers that three waves per SIMD leave.
-template <class T, bool DBG, bool ROUNDS, bool DIN = false, int NW = kBwdWaves>
+template <class T, bool DBG, bool ROUNDS, bool DIN = false, int NW = kBwdWaves, bool SHARE = false>
 __global__ __launch_bounds__(NW * 64) void bwd_partials_kernel(
     int B, int K, int SH2, int NG, int NB, int P, int UPW,
     const T* __restrict__ H, const T* __restrict__ hs2,
@@ -1296,7 +1300,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_partials_kernel(
   // each unit's registers keep one role.
   BwdUnit R0, R1;
   int u = wave;
-  bwd_load<ROUNDS>(R0, min(u, n - 1), c, lane);
+  bwd_load<ROUNDS, SHARE>(R0, min(u, n - 1), c, lane);
   float* sW = &sRed[0][0] + NW * kFusedTile;         // DIN: staged weights
   float* tile = &sRed[0][0] + wave * kFusedTile;     // DIN: this wave's tile
   if constexpr (DIN) {
@@ -1327,14 +1331,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_partials_kernel(
   }
   for (; u < n; u += 2 * S) {
     float dv[2][4];
-    bwd_load<ROUNDS>(R1, min(u + S, n - 1), c, lane);
+    bwd_load<ROUNDS, SHARE>(R1, min(u + S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
     bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg, dv);
     if constexpr (DIN) {
       din_fused(dv, R0.t == K, u < n, R0.blk, R0.t, B, K, SH2, jb, kg, m, lane, tile, sW, dH, dhs2);
       __builtin_amdgcn_sched_barrier(0);  // the next unit's loads stay after (registers)
     }
-    bwd_load<ROUNDS>(R0, min(u + 2 * S, n - 1), c, lane);
+    bwd_load<ROUNDS, SHARE>(R0, min(u + 2 * S, n - 1), c, lane);
     __builtin_amdgcn_sched_barrier(0);
     bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg, dv);
     if constexpr (DIN) {
@@ -2167,8 +2171,16 @@ void launch_partials(const Plan& pl, const T* H, const T* hs2, const void* saved
   const int grid = 8 * pl.V * ((pl.P + 7) / 8);
   const bool dbg = da || db || dc, rounds = pl.K > kChunk;
   constexpr int NWD = sizeof(T) == 4 ? 8 : kBwdWaves;  // waves of the DIN form
+  // several state groups: the slice's history tiles are shared through L2
+  // (wide state, backward partials 432 -> 405 us; the one-group pages' shape
+  // keeps the streaming hint, 20.0 vs 22.0 us)
+  const bool share = pl.NG > 1;
   auto kern = din ? (rounds ? bwd_partials_kernel<T, false, true, true, NWD>
                             : bwd_partials_kernel<T, false, false, true, NWD>)
+              : share ? (dbg ? (rounds ? bwd_partials_kernel<T, true, true, false, kBwdWaves, true>
+                                       : bwd_partials_kernel<T, true, false, false, kBwdWaves, true>)
+                             : (rounds ? bwd_partials_kernel<T, false, true, false, kBwdWaves, true>
+                                       : bwd_partials_kernel<T, false, false, false, kBwdWaves, true>))
               : dbg ? (rounds ? bwd_partials_kernel<T, true, true> : bwd_partials_kernel<T, true, false>)
                     : (rounds ? bwd_partials_kernel<T, false, true> : bwd_partials_kernel<T, false, false>);
   const int threads = (din ? NWD : kBwdWaves) * 64;
