@@ -36,7 +36,10 @@
 //    (64-feature column block, state group, range of sample blocks); its 12
 //    waves take (sample block, history step) units round-robin and accumulate
 //    H^T [d_a | d_b] and h_s2^T d_c with MFMA (M = features, N = states,
-//    K = rows) in registers.  The waves' partials are summed in LDS in a fixed
+//    K = rows) in registers: fp32 MFMAs with one state group, split-bf16
+//    MFMAs over pairs of steps with several (where the four state groups'
+//    work-groups make the contraction bound by the matrix cores and the
+//    VALU).  The waves' partials are summed in LDS in a fixed
 //    order and written as one slice.  Work-groups that share rows are placed
 //    on the same XCD (dispatch is round-robin over the 8 XCDs) so the shared
 //    saved/d_context reads hit that XCD's L2.
@@ -74,6 +77,7 @@ constexpr int kFwdPairPrefetch = 4;  // bf16 history loads (64 features of 8 row
 constexpr int kRegRounds = 8;      // rounds whose gate product the forward keeps in registers
 constexpr int kFwdChunkTarget = 512;  // forward work-groups a chunked history aims for
 constexpr int kBwdWaves = 12;
+constexpr int kBwdPairWaves = 8;  // paired-step units (STATE_D >= 32): two units of registers per wave
 constexpr int kBwdTargetGroups = 256;  // backward work-groups to aim for (one per CU)
 constexpr int kRedThreads = 256;
 constexpr int kRedQuads = 32;      // output float4s per reduce work-group
@@ -933,7 +937,8 @@ __global__ __launch_bounds__(kCarryThreads) void fwd_carry_kernel(int NBG, int K
 // Backward, phase 1: split-K partial products.
 //   grid = 8 * V * ceil(P / 8), V = (SH2/64) * NG variants, 768 threads
 //   (12 waves: three per SIMD, for the matrix cores to have work while
-//   other waves wait for memory).
+//   other waves wait for memory); 512 threads with paired steps (below),
+//   whose units hold twice the registers.
 // Work-group w: XCD w % 8, variant v = (w/8) % V (column block jb, state
 // group sg), slice p = ((w/8) / V) * 8 + w % 8 covering units
 // [p*UPW, min(NB*(K+1), (p+1)*UPW)), unit u = (block u / (K+1), step u % (K+1)),
@@ -969,6 +974,7 @@ struct BwdUnit {
 template <class T>
 struct BwdCtx {
   int B, K, SH2, D, NG, sg, u0, kg, state;
+  int UPB;  // units per sample block: K steps (or ceil(K/2) step pairs) and the readout
   const T* H;
   const T* hs2;
   const float* saved;
@@ -987,17 +993,13 @@ struct BwdCtx {
 // the compiler's memory-counter waits stay exact, so the next unit's loads
 // (issued before this unit is consumed) stay in flight.  Rows of samples past
 // B (last block only) re-read a valid row; their d_context is masked to zero.
-// SHARE (several state groups): the work-groups of a slice's column block,
-// one per state group, read the same history tiles on one XCD, so those
-// loads go through L2 as ordinary loads; with one state group each tile is
-// read once and streams with the non-temporal hint.
-template <bool ROUNDS, bool SHARE, class T>
+template <bool ROUNDS, class T>
 __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, int lane) {
   // unit u of the work-group's slice: block and step (t == K: the readout)
   const int ug = c.u0 + u;
   BwdUnit& q = U;
-  q.blk = ug / (c.K + 1);
-  q.t = ug - q.blk * (c.K + 1);
+  q.blk = ug / c.UPB;
+  q.t = ug - q.blk * c.UPB;
   q.nvalid = c.B - q.blk * kBlock;
   const bool step = q.t < c.K;
   const float* sv = c.saved + ((size_t)q.blk * c.NG + c.sg) * c.blk_stride;
@@ -1018,9 +1020,9 @@ __device__ __forceinline__ void bwd_load(BwdUnit& U, int u, const BwdCtx<T>& c, 
     const bool ok = 4 * c.kg + i < q.nvalid;
     const T* hp = rows + (size_t)s0 * rstride + (ok ? hk : 0) + c.col;
     if constexpr (sizeof(T) == 2)
-      U.hr[i] = SHARE ? *reinterpret_cast<const v2u*>(hp) : __builtin_nontemporal_load(reinterpret_cast<const v2u*>(hp));
+      U.hr[i] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(hp));
     else
-      U.h[i] = SHARE ? ld4(reinterpret_cast<const float*>(hp)) : ld4_in(hp);
+      U.h[i] = ld4_in(hp);
     U.dc[i] = c.dctx[(size_t)s0 * c.D + (ok ? 4 * c.kg * c.D : 0) + c.state];
   }
 }
@@ -1147,6 +1149,161 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
   }
 }
 
+// Paired steps (several state groups, STATE_D >= 32).  There the fp32 MFMAs
+// of the partials took half the kernel's time (the state groups' work-groups
+// multiply the same history tiles, one per group), so a unit takes two
+// history steps t0, t0+1 of its sample block and feeds
+// v_mfma_f32_16x16x32_bf16 with K = 32 (sample, step) rows: row
+// kappa = 8kg + 4s + i is sample 4kg+i at step t0+s, which is exactly what
+// lane (kg, m) loads (A: its four rows at both steps; B: its d values at
+// both steps).  fp32 history values and the d values are split exactly into
+// three bf16 terms, and the six term products whose indices sum to at most
+// 2 accumulate in fp32 (the three dropped ones are below 2^-23 of the
+// product together, about one fp32 rounding); bf16 history values are
+// exact, so three products.  The result layout is that of the fp32 MFMAs.
+// Units per sample block: ceil(K/2) step pairs and the readout (its second
+// half carries d = 0).  A pair past the last step (odd K) re-reads step t0
+// with d masked to zero.  The history tiles are ordinary loads: the state
+// groups' work-groups of a column block read them on one XCD and share them
+// through L2.  32768 samples, K = 8, SH2 = 512, STATE_D = 64: 400-403 ->
+// 333-337 us.  What remains is mostly VALU (the splits, the d values, load
+// addresses) and memory: with the MFMAs taken out the kernel still took
+// 289 us where it took 351-361 us on the same machine.
+struct BwdPair {
+  v4f h[2][4];   // A operands: step s, row i (sample 4kg+i), 4 features
+  v2u hr[2][4];  // bf16 inputs: the same, as loaded
+  v4f al[2];     // alpha'_t of each step (readout: x_K)
+  v4f be[2];     // beta'_t of each step
+  v4f sr;        // S_r of the pair's round (both steps share it: rounds are 8 steps)
+  float dc[4];   // d_context of samples 4kg+i, state n (unmasked)
+  int blk, tp, nvalid;  // block, pair (tp == ceil(K/2): readout), samples below B
+};
+
+template <bool ROUNDS, class T>
+__device__ __forceinline__ void bwd_load_pair(BwdPair& U, int u, const BwdCtx<T>& c, int lane) {
+  const int ug = c.u0 + u;
+  const int KP = c.UPB - 1;
+  U.blk = ug / c.UPB;
+  U.tp = ug - U.blk * c.UPB;
+  U.nvalid = c.B - U.blk * kBlock;
+  const bool step = U.tp < KP;
+  const int t0 = 2 * U.tp;
+  const int t1 = step && t0 + 1 < c.K ? t0 + 1 : t0;
+  const float* sv = c.saved + ((size_t)U.blk * c.NG + c.sg) * c.blk_stride;
+  const int pl[4] = {step ? 2 * t0 : 2 * c.K, step ? 2 * t0 + 1 : 2 * c.K, step ? 2 * t1 : 2 * c.K,
+                     step ? 2 * t1 + 1 : 2 * c.K};
+  U.al[0] = ld4(sv + (size_t)pl[0] * kPlane + 4 * lane);
+  U.be[0] = ld4(sv + (size_t)pl[1] * kPlane + 4 * lane);
+  U.al[1] = ld4(sv + (size_t)pl[2] * kPlane + 4 * lane);
+  U.be[1] = ld4(sv + (size_t)pl[3] * kPlane + 4 * lane);
+  if constexpr (ROUNDS) {
+    const int ps = step ? 2 * c.K + 1 + t0 / kChunk : 2 * c.K;
+    U.sr = ld4(sv + (size_t)ps * kPlane + 4 * lane);
+  }
+  const T* rows0 = step ? c.H + (size_t)t0 * c.SH2 : c.hs2;
+  const T* rows1 = step ? c.H + (size_t)t1 * c.SH2 : c.hs2;
+  const size_t rstride = step ? (size_t)c.K * c.SH2 : (size_t)c.SH2;
+  const long long hk = step ? c.hk_step : c.hk_out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s0 = min(U.blk * kBlock + i, c.B - 1);
+    const bool ok = 4 * c.kg + i < U.nvalid;
+    const size_t off = (size_t)s0 * rstride + (ok ? hk : 0) + c.col;
+    if constexpr (sizeof(T) == 2) {
+      U.hr[0][i] = *reinterpret_cast<const v2u*>(rows0 + off);
+      U.hr[1][i] = *reinterpret_cast<const v2u*>(rows1 + off);
+    } else {
+      U.h[0][i] = ld4(reinterpret_cast<const float*>(rows0 + off));
+      U.h[1][i] = ld4(reinterpret_cast<const float*>(rows1 + off));
+    }
+    U.dc[i] = c.dctx[(size_t)s0 * c.D + (ok ? 4 * c.kg * c.D : 0) + c.state];
+  }
+}
+
+template <bool DBG, bool ROUNDS, class T>
+__device__ __forceinline__ void bwd_compute_pair(const BwdPair& U, bool live, const BwdCtx<T>& c, v4f (&acc)[4][3],
+                                                 float* __restrict__ d_a_out, float* __restrict__ d_b_out,
+                                                 float* __restrict__ d_c_out, bool write_dbg) {
+  constexpr bool BF = sizeof(T) == 2;
+  const int KP = c.UPB - 1;
+  const bool step = U.tp < KP;
+  const int t0 = 2 * U.tp;
+  const bool two = step && t0 + 1 < c.K;
+  const int sbase = U.blk * kBlock + 4 * c.kg;
+  // d values, kappa order (4s + i); the readout's second half is zero
+  float da[8], db[8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = live && 4 * c.kg + i < U.nvalid && (s == 0 || two);
+      const float dcs = ok ? (ROUNDS && step ? U.dc[i] * U.sr[i] : U.dc[i]) : 0.f;
+      da[4 * s + i] = dcs * U.al[s][i];
+      db[4 * s + i] = dcs * U.be[s][i];
+      if (DBG && write_dbg && ok) {
+        const int smp = sbase + i;
+        if (step) {
+          if (d_a_out) d_a_out[((size_t)smp * c.K + t0 + s) * c.D + c.state] = da[4 * s + i];
+          if (d_b_out) d_b_out[((size_t)smp * c.K + t0 + s) * c.D + c.state] = db[4 * s + i];
+        } else if (s == 0 && d_c_out) {
+          d_c_out[(size_t)smp * c.D + c.state] = da[i];
+        }
+      }
+    }
+  // A operand of tile qq: feature 4m+qq at the eight (sample, step) rows
+  auto hist = [&](int qq, v8bf (&xa)[BF ? 1 : 3]) {
+    if constexpr (BF) {
+      const int w = qq >> 1;
+      const unsigned sel = (qq & 1) ? 0x07060302u : 0x05040100u;
+      v4u p;
+      p[0] = __builtin_amdgcn_perm(U.hr[0][1][w], U.hr[0][0][w], sel);
+      p[1] = __builtin_amdgcn_perm(U.hr[0][3][w], U.hr[0][2][w], sel);
+      p[2] = __builtin_amdgcn_perm(U.hr[1][1][w], U.hr[1][0][w], sel);
+      p[3] = __builtin_amdgcn_perm(U.hr[1][3][w], U.hr[1][2][w], sel);
+      xa[0] = __builtin_bit_cast(v8bf, p);
+    } else {
+      float x[8];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * s + i] = U.h[s][i][qq];
+      split3_v8(x, xa);
+    }
+  };
+  // term products (history term th, d term td) with th + td <= 2, the
+  // smaller ones first; the step/readout choice is taken once per unit
+  if (step) {
+    v8bf ta[3], tb[3];
+    split3_v8(da, ta);
+    split3_v8(db, tb);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      v8bf xa[BF ? 1 : 3];
+      hist(qq, xa);
+#pragma unroll
+      for (int td = 2; td >= 0; --td)
+#pragma unroll
+        for (int th = (BF ? 0 : 2 - td); th >= 0; --th) {
+          acc[qq][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[th], ta[td], acc[qq][0], 0, 0, 0);
+          acc[qq][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[th], tb[td], acc[qq][1], 0, 0, 0);
+        }
+    }
+  } else {
+    v8bf ta[3];
+    split3_v8(da, ta);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      v8bf xa[BF ? 1 : 3];
+      hist(qq, xa);
+#pragma unroll
+      for (int td = 2; td >= 0; --td)
+#pragma unroll
+        for (int th = (BF ? 0 : 2 - td); th >= 0; --th)
+          acc[qq][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[th], ta[td], acc[qq][2], 0, 0, 0);
+    }
+  }
+}
+
 // Input gradients inside the backward (STATE_D = 16: the work-group's state
 // group is every state).  A unit's d_h tile -- its 16 samples at this column
 // block's 64 features -- is
@@ -1236,7 +1393,7 @@ __device__ __forceinline__ void din_fused(const float (&dv)[2][4], bool readout,
 // the LDS of the final slice sum.
 // NW waves per work-group: kBwdWaves, or 8 for the fp32 DIN form, which
 // needs more than the 168 registers that three waves per SIMD leave.
-template <class T, bool DBG, bool ROUNDS, bool DIN = false, int NW = kBwdWaves, bool SHARE = false>
+template <class T, bool DBG, bool ROUNDS, bool DIN = false, int NW = kBwdWaves, bool PS = false>
 __global__ __launch_bounds__(NW * 64) void bwd_partials_kernel(
     int B, int K, int SH2, int NG, int NB, int P, int UPW,
     const T* __restrict__ H, const T* __restrict__ hs2,
@@ -1283,7 +1440,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_partials_kernel(
   c.rounds = K > kChunk;
   c.hk_step = 4LL * kg * K * SH2;
   c.hk_out = 4LL * kg * SH2;
-  const int n = min(NB * (K + 1) - c.u0, UPW);
+  c.UPB = PS ? (K + 1) / 2 + 1 : K + 1;
+  const int n = min(NB * c.UPB - c.u0, UPW);
 
   v4f acc[4][3];
 #pragma unroll
@@ -1292,58 +1450,73 @@ __global__ __launch_bounds__(NW * 64) void bwd_partials_kernel(
     for (int pl = 0; pl < 3; ++pl) acc[q][pl] = v4f{0.f, 0.f, 0.f, 0.f};
 
   constexpr int S = NW;
-  // Two-unit ring.  Requests are unconditional: past the last unit a wave
-  // re-loads the last unit (unused), so the compiler's waits stay exact.
-  // Both halves of an iteration always run: a unit past the last one (u >= n)
-  // re-reads and re-multiplies the last unit with its d_context masked to
-  // zero, so the loop has no data-dependent exit between the two halves and
-  // each unit's registers keep one role.
-  BwdUnit R0, R1;
-  int u = wave;
-  bwd_load<ROUNDS, SHARE>(R0, min(u, n - 1), c, lane);
-  float* sW = &sRed[0][0] + NW * kFusedTile;         // DIN: staged weights
-  float* tile = &sRed[0][0] + wave * kFusedTile;     // DIN: this wave's tile
-  if constexpr (DIN) {
-    // W of this column block as v_mfma_f32_16x16x32_bf16 A operands, three
-    // exact bf16 terms each: entry (jt, lane (kg, m)) holds row jb*64 +
-    // jt*16 + m at kappa = 8kg .. 8kg+7, W_A below 16 and W_B above for the
-    // steps, W_C below 16 and zeros above for the readout
-    for (int e = tid; e < 2 * 4 * 64; e += NW * 64) {
-      const bool ro = e >= 4 * 64;
-      const int l = e & 63, jt = (e >> 6) & 3, kgw = l >> 4;
-      const float* row = (ro ? WC : (kgw < 2 ? WA : WB)) + (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * kGroup +
-                         8 * (kgw & 1);
-      const v4f a = ld4(row), b = ld4(row + 4);
-      const bool zero = ro && kgw >= 2;
-      float v[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[k] = zero ? 0.f : a[k];
-        v[4 + k] = zero ? 0.f : b[k];
-      }
-      v8bf tw[3];
-      split3_v8(v, tw);
-      v4u* dst = reinterpret_cast<v4u*>(sW) + (ro ? 4 * 3 * 64 : 0);
-#pragma unroll
-      for (int tm = 0; tm < 3; ++tm) dst[(jt * 3 + tm) * 64 + l] = __builtin_bit_cast(v4u, tw[tm]);
-    }
-    __syncthreads();
-  }
-  for (; u < n; u += 2 * S) {
-    float dv[2][4];
-    bwd_load<ROUNDS, SHARE>(R1, min(u + S, n - 1), c, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg, dv);
-    if constexpr (DIN) {
-      din_fused(dv, R0.t == K, u < n, R0.blk, R0.t, B, K, SH2, jb, kg, m, lane, tile, sW, dH, dhs2);
-      __builtin_amdgcn_sched_barrier(0);  // the next unit's loads stay after (registers)
-    }
-    bwd_load<ROUNDS, SHARE>(R0, min(u + 2 * S, n - 1), c, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg, dv);
-    if constexpr (DIN) {
-      din_fused(dv, R1.t == K, u + S < n, R1.blk, R1.t, B, K, SH2, jb, kg, m, lane, tile, sW, dH, dhs2);
+  if constexpr (PS) {
+    // the same two-unit ring over step pairs
+    BwdPair R0, R1;
+    int u = wave;
+    bwd_load_pair<ROUNDS>(R0, min(u, n - 1), c, lane);
+    for (; u < n; u += 2 * S) {
+      bwd_load_pair<ROUNDS>(R1, min(u + S, n - 1), c, lane);
       __builtin_amdgcn_sched_barrier(0);
+      bwd_compute_pair<DBG, ROUNDS>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+      bwd_load_pair<ROUNDS>(R0, min(u + 2 * S, n - 1), c, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      bwd_compute_pair<DBG, ROUNDS>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
+    }
+  } else {
+    // Two-unit ring.  Requests are unconditional: past the last unit a wave
+    // re-loads the last unit (unused), so the compiler's waits stay exact.
+    // Both halves of an iteration always run: a unit past the last one (u >= n)
+    // re-reads and re-multiplies the last unit with its d_context masked to
+    // zero, so the loop has no data-dependent exit between the two halves and
+    // each unit's registers keep one role.
+    BwdUnit R0, R1;
+    int u = wave;
+    bwd_load<ROUNDS>(R0, min(u, n - 1), c, lane);
+    float* sW = &sRed[0][0] + NW * kFusedTile;         // DIN: staged weights
+    float* tile = &sRed[0][0] + wave * kFusedTile;     // DIN: this wave's tile
+    if constexpr (DIN) {
+      // W of this column block as v_mfma_f32_16x16x32_bf16 A operands, three
+      // exact bf16 terms each: entry (jt, lane (kg, m)) holds row jb*64 +
+      // jt*16 + m at kappa = 8kg .. 8kg+7, W_A below 16 and W_B above for the
+      // steps, W_C below 16 and zeros above for the readout
+      for (int e = tid; e < 2 * 4 * 64; e += NW * 64) {
+        const bool ro = e >= 4 * 64;
+        const int l = e & 63, jt = (e >> 6) & 3, kgw = l >> 4;
+        const float* row = (ro ? WC : (kgw < 2 ? WA : WB)) + (size_t)(jb * kColBlock + jt * 16 + (l & 15)) * kGroup +
+                           8 * (kgw & 1);
+        const v4f a = ld4(row), b = ld4(row + 4);
+        const bool zero = ro && kgw >= 2;
+        float v[8];
+  #pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[k] = zero ? 0.f : a[k];
+          v[4 + k] = zero ? 0.f : b[k];
+        }
+        v8bf tw[3];
+        split3_v8(v, tw);
+        v4u* dst = reinterpret_cast<v4u*>(sW) + (ro ? 4 * 3 * 64 : 0);
+  #pragma unroll
+        for (int tm = 0; tm < 3; ++tm) dst[(jt * 3 + tm) * 64 + l] = __builtin_bit_cast(v4u, tw[tm]);
+      }
+      __syncthreads();
+    }
+    for (; u < n; u += 2 * S) {
+      float dv[2][4];
+      bwd_load<ROUNDS>(R1, min(u + S, n - 1), c, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg, dv);
+      if constexpr (DIN) {
+        din_fused(dv, R0.t == K, u < n, R0.blk, R0.t, B, K, SH2, jb, kg, m, lane, tile, sW, dH, dhs2);
+        __builtin_amdgcn_sched_barrier(0);  // the next unit's loads stay after (registers)
+      }
+      bwd_load<ROUNDS>(R0, min(u + 2 * S, n - 1), c, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      bwd_compute<DBG, ROUNDS, sizeof(T) == 2>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg, dv);
+      if constexpr (DIN) {
+        din_fused(dv, R1.t == K, u + S < n, R1.blk, R1.t, B, K, SH2, jb, kg, m, lane, tile, sW, dH, dhs2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   // DIN: every wave is done with its tile and the staged W before sRed
@@ -2031,10 +2204,13 @@ int make_plan(int B, int K, int SH2, int D, Plan* pl) {
   pl->NJB = SH2 / kColBlock;
   pl->V = pl->NJB * pl->NG;
   // Backward slices: about kBwdTargetGroups work-groups over the V variants,
-  // each slice at least one unit per wave.
-  const int units = pl->NB * (K + 1);
+  // each slice at least one unit per wave.  Several state groups take step
+  // pairs (ceil(K/2) units and the readout per sample block).
+  const bool paired = pl->NG > 1;
+  const int waves = paired ? kBwdPairWaves : kBwdWaves;
+  const int units = pl->NB * (paired ? (K + 1) / 2 + 1 : K + 1);
   int p0 = (kBwdTargetGroups + pl->V - 1) / pl->V;
-  if (p0 > (units + kBwdWaves - 1) / kBwdWaves) p0 = (units + kBwdWaves - 1) / kBwdWaves;
+  if (p0 > (units + waves - 1) / waves) p0 = (units + waves - 1) / waves;
   pl->UPW = (units + p0 - 1) / p0;
   pl->P = (units + pl->UPW - 1) / pl->UPW;
   pl->saved_bytes = (size_t)pl->NB * pl->NG * (size_t)saved_planes(K) * kPlane * sizeof(float);
@@ -2171,19 +2347,19 @@ void launch_partials(const Plan& pl, const T* H, const T* hs2, const void* saved
   const int grid = 8 * pl.V * ((pl.P + 7) / 8);
   const bool dbg = da || db || dc, rounds = pl.K > kChunk;
   constexpr int NWD = sizeof(T) == 4 ? 8 : kBwdWaves;  // waves of the DIN form
-  // several state groups: the slice's history tiles are shared through L2
-  // (wide state, backward partials 432 -> 405 us; the one-group pages' shape
-  // keeps the streaming hint, 20.0 vs 22.0 us)
-  const bool share = pl.NG > 1;
+  // several state groups: step pairs on bf16 matrix cores, history tiles
+  // shared through L2
+  const bool paired = pl.NG > 1;
+  constexpr int NWP = kBwdPairWaves;
   auto kern = din ? (rounds ? bwd_partials_kernel<T, false, true, true, NWD>
                             : bwd_partials_kernel<T, false, false, true, NWD>)
-              : share ? (dbg ? (rounds ? bwd_partials_kernel<T, true, true, false, kBwdWaves, true>
-                                       : bwd_partials_kernel<T, true, false, false, kBwdWaves, true>)
-                             : (rounds ? bwd_partials_kernel<T, false, true, false, kBwdWaves, true>
-                                       : bwd_partials_kernel<T, false, false, false, kBwdWaves, true>))
+              : paired ? (dbg ? (rounds ? bwd_partials_kernel<T, true, true, false, NWP, true>
+                                        : bwd_partials_kernel<T, true, false, false, NWP, true>)
+                              : (rounds ? bwd_partials_kernel<T, false, true, false, NWP, true>
+                                        : bwd_partials_kernel<T, false, false, false, NWP, true>))
               : dbg ? (rounds ? bwd_partials_kernel<T, true, true> : bwd_partials_kernel<T, true, false>)
                     : (rounds ? bwd_partials_kernel<T, false, true> : bwd_partials_kernel<T, false, false>);
-  const int threads = (din ? NWD : kBwdWaves) * 64;
+  const int threads = (din ? NWD : paired ? NWP : kBwdWaves) * 64;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, pl.B, pl.K, pl.SH2, pl.NG,
                      pl.NB, pl.P, pl.UPW, H, hs2, static_cast<const float*>(saved), dctx, da, db, dc,
                      static_cast<float*>(ws), WA, WB, WC, dH, dhs2);
