@@ -1166,9 +1166,9 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
 // with d masked to zero.  The history tiles are ordinary loads: the state
 // groups' work-groups of a column block read them on one XCD and share them
 // through L2.  32768 samples, K = 8, SH2 = 512, STATE_D = 64: 400-403 ->
-// 333-337 us.  What remains is mostly VALU (the splits, the d values, load
-// addresses) and memory: with the MFMAs taken out the kernel still took
-// 289 us where it took 351-361 us on the same machine.
+// 333-337 us.  What remains is mostly VALU (the splits, the d values) and
+// memory: with the MFMAs taken out the kernel still took 289 us where it
+// took 351-361 us on the same machine.
 struct BwdPair {
   v4f h[2][4];   // A operands: step s, row i (sample 4kg+i), 4 features
   v2u hr[2][4];  // bf16 inputs: the same, as loaded
@@ -1179,44 +1179,75 @@ struct BwdPair {
   int blk, tp, nvalid;  // block, pair (tp == ceil(K/2): readout), samples below B
 };
 
+// Buffer loads with per-lane byte offsets fixed for the work-group: a unit
+// changes only scalar descriptors (base and size), so its loads cost no
+// VALU address arithmetic.  Each descriptor ends at the block's last sample
+// below B, so rows past B read as zeros (history and d_context alike) and
+// contribute nothing.  The offsets stay below 2^32 for K * SH2 <= 2^26.
+struct PairLane {
+  unsigned hs[4];  // history row 4kg+i of a block (step units), this lane's features
+  unsigned ho[4];  // h_s2 row 4kg+i (readout units)
+  unsigned dc[4];  // d_context row 4kg+i, this lane's state
+  unsigned pl;     // this lane's float4 of a saved plane
+};
+template <class T>
+__device__ __forceinline__ PairLane pair_lane(const BwdCtx<T>& c, int lane) {
+  PairLane L;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned r = 4 * c.kg + i;
+    L.hs[i] = (unsigned)(((size_t)r * c.K * c.SH2 + c.col) * sizeof(T));
+    L.ho[i] = (unsigned)(((size_t)r * c.SH2 + c.col) * sizeof(T));
+    L.dc[i] = (r * c.D + c.state) * sizeof(float);
+  }
+  L.pl = 16u * lane;
+  return L;
+}
+__device__ __forceinline__ v4f ldb4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 template <bool ROUNDS, class T>
-__device__ __forceinline__ void bwd_load_pair(BwdPair& U, int u, const BwdCtx<T>& c, int lane) {
+__device__ __forceinline__ void bwd_load_pair(BwdPair& U, int u, const BwdCtx<T>& c, const PairLane& L) {
   const int ug = c.u0 + u;
   const int KP = c.UPB - 1;
   U.blk = ug / c.UPB;
   U.tp = ug - U.blk * c.UPB;
   U.nvalid = c.B - U.blk * kBlock;
+  const int nv = min(U.nvalid, kBlock);
   const bool step = U.tp < KP;
   const int t0 = 2 * U.tp;
-  const int t1 = step && t0 + 1 < c.K ? t0 + 1 : t0;
-  const float* sv = c.saved + ((size_t)U.blk * c.NG + c.sg) * c.blk_stride;
-  const int pl[4] = {step ? 2 * t0 : 2 * c.K, step ? 2 * t0 + 1 : 2 * c.K, step ? 2 * t1 : 2 * c.K,
-                     step ? 2 * t1 + 1 : 2 * c.K};
-  U.al[0] = ld4(sv + (size_t)pl[0] * kPlane + 4 * lane);
-  U.be[0] = ld4(sv + (size_t)pl[1] * kPlane + 4 * lane);
-  U.al[1] = ld4(sv + (size_t)pl[2] * kPlane + 4 * lane);
-  U.be[1] = ld4(sv + (size_t)pl[3] * kPlane + 4 * lane);
-  if constexpr (ROUNDS) {
-    const int ps = step ? 2 * c.K + 1 + t0 / kChunk : 2 * c.K;
-    U.sr = ld4(sv + (size_t)ps * kPlane + 4 * lane);
-  }
-  const T* rows0 = step ? c.H + (size_t)t0 * c.SH2 : c.hs2;
-  const T* rows1 = step ? c.H + (size_t)t1 * c.SH2 : c.hs2;
-  const size_t rstride = step ? (size_t)c.K * c.SH2 : (size_t)c.SH2;
-  const long long hk = step ? c.hk_step : c.hk_out;
+  // the pair's second step, when there is one (read as a scalar: the
+  // descriptors below must stay in scalar registers)
+  const int dt = __builtin_amdgcn_readfirstlane(step && t0 + 1 < c.K ? 1 : 0);
+  const __amdgpu_buffer_rsrc_t rp =
+      make_rsrc(c.saved + ((size_t)U.blk * c.NG + c.sg) * c.blk_stride, (unsigned)(c.blk_stride * sizeof(float)));
+  constexpr unsigned PB = kPlane * sizeof(float);
+  const unsigned p0 = step ? 2 * t0 : 2 * c.K;
+  const unsigned p1 = step ? 2 * (t0 + dt) : 2 * c.K;
+  U.al[0] = ldb4(rp, L.pl, p0 * PB);
+  U.be[0] = ldb4(rp, L.pl, (step ? p0 + 1 : p0) * PB);
+  U.al[1] = ldb4(rp, L.pl, p1 * PB);
+  U.be[1] = ldb4(rp, L.pl, (step ? p1 + 1 : p1) * PB);
+  if constexpr (ROUNDS) U.sr = ldb4(rp, L.pl, (step ? 2 * c.K + 1 + t0 / kChunk : 2 * c.K) * PB);
+  // rows of the block at step t0 (or its h_s2 rows): the last valid row ends
+  // after the pair's span
+  const size_t rs = step ? (size_t)c.K * c.SH2 : (size_t)c.SH2;
+  const T* base = step ? c.H + ((size_t)U.blk * kBlock * c.K + t0) * c.SH2 : c.hs2 + (size_t)U.blk * kBlock * c.SH2;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(base, (unsigned)(((size_t)(nv - 1) * rs + (size_t)(dt + 1) * c.SH2) * sizeof(T)));
+  const unsigned s1 = (unsigned)(dt * c.SH2 * sizeof(T));
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(c.dctx + (size_t)U.blk * kBlock * c.D, (unsigned)(nv * c.D * sizeof(float)));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int s0 = min(U.blk * kBlock + i, c.B - 1);
-    const bool ok = 4 * c.kg + i < U.nvalid;
-    const size_t off = (size_t)s0 * rstride + (ok ? hk : 0) + c.col;
+    const unsigned off = step ? L.hs[i] : L.ho[i];
     if constexpr (sizeof(T) == 2) {
-      U.hr[0][i] = *reinterpret_cast<const v2u*>(rows0 + off);
-      U.hr[1][i] = *reinterpret_cast<const v2u*>(rows1 + off);
+      U.hr[0][i] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rh, off, 0, 0));
+      U.hr[1][i] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rh, off, s1, 0));
     } else {
-      U.h[0][i] = ld4(reinterpret_cast<const float*>(rows0 + off));
-      U.h[1][i] = ld4(reinterpret_cast<const float*>(rows1 + off));
+      U.h[0][i] = ldb4(rh, off, 0);
+      U.h[1][i] = ldb4(rh, off, s1);
     }
-    U.dc[i] = c.dctx[(size_t)s0 * c.D + (ok ? 4 * c.kg * c.D : 0) + c.state];
+    U.dc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, L.dc[i], 0, 0));
   }
 }
 
@@ -1236,11 +1267,12 @@ __device__ __forceinline__ void bwd_compute_pair(const BwdPair& U, bool live, co
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = live && 4 * c.kg + i < U.nvalid && (s == 0 || two);
-      const float dcs = ok ? (ROUNDS && step ? U.dc[i] * U.sr[i] : U.dc[i]) : 0.f;
+      // rows past B arrive with d_context = 0
+      const bool use = live && (s == 0 || two);
+      const float dcs = use ? (ROUNDS && step ? U.dc[i] * U.sr[i] : U.dc[i]) : 0.f;
       da[4 * s + i] = dcs * U.al[s][i];
       db[4 * s + i] = dcs * U.be[s][i];
-      if (DBG && write_dbg && ok) {
+      if (DBG && write_dbg && use && 4 * c.kg + i < U.nvalid) {
         const int smp = sbase + i;
         if (step) {
           if (d_a_out) d_a_out[((size_t)smp * c.K + t0 + s) * c.D + c.state] = da[4 * s + i];
@@ -1453,13 +1485,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_partials_kernel(
   if constexpr (PS) {
     // the same two-unit ring over step pairs
     BwdPair R0, R1;
+    const PairLane L = pair_lane(c, lane);
     int u = wave;
-    bwd_load_pair<ROUNDS>(R0, min(u, n - 1), c, lane);
+    bwd_load_pair<ROUNDS>(R0, min(u, n - 1), c, L);
     for (; u < n; u += 2 * S) {
-      bwd_load_pair<ROUNDS>(R1, min(u + S, n - 1), c, lane);
+      bwd_load_pair<ROUNDS>(R1, min(u + S, n - 1), c, L);
       __builtin_amdgcn_sched_barrier(0);
       bwd_compute_pair<DBG, ROUNDS>(R0, u < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
-      bwd_load_pair<ROUNDS>(R0, min(u + 2 * S, n - 1), c, lane);
+      bwd_load_pair<ROUNDS>(R0, min(u + 2 * S, n - 1), c, L);
       __builtin_amdgcn_sched_barrier(0);
       bwd_compute_pair<DBG, ROUNDS>(R1, u + S < n, c, acc, d_a_out, d_b_out, d_c_out, write_dbg);
     }
@@ -2318,9 +2351,14 @@ void launch_fwd(const Plan& pl, const T* H, const T* hs2, const float* WA, const
   }
 }
 
+// Several state groups: the backward addresses a 16-sample block's rows with
+// 32-bit buffer offsets, so they must span less than 4 GiB.
+bool bwd_rows_fit(const Plan& pl) { return pl.NG == 1 || (long long)pl.K * pl.SH2 <= kDinMaxRowFloats; }
+
 int check_bwd_common(const Plan& pl, const void* H, const void* hs2, const void* saved, size_t saved_bytes,
                      const float* dctx, const float* da, const float* db, const float* dc, const void* ws,
                      size_t ws_bytes) {
+  if (!bwd_rows_fit(pl)) return MAMBA2_SCAN_EUNSUPPORTED;
   if (!H || !hs2 || !saved || !dctx || !ws) return MAMBA2_SCAN_ENULL;
   if (saved_bytes < pl.saved_bytes || ws_bytes < pl.ws_bytes) return MAMBA2_SCAN_ESIZE;
   if (!aligned16(H) || !aligned16(hs2) || !aligned16(saved) || !aligned16(ws) || !aligned4(dctx))
@@ -2493,6 +2531,7 @@ int scratch_address(void** out) {
 int check_bwd_noalloc(const Plan& pl, const void* H, const void* hs2, const void* saved, size_t saved_bytes,
                       const float* dctx, const float* dWA, const float* dWB, const float* dWC, const float* da,
                       const float* db, const float* dc) {
+  if (!bwd_rows_fit(pl)) return MAMBA2_SCAN_EUNSUPPORTED;
   if (!H || !hs2 || !saved || !dctx || !dWA || !dWB || !dWC) return MAMBA2_SCAN_ENULL;
   if (saved_bytes < pl.saved_bytes) return MAMBA2_SCAN_ESIZE;
   if (pl.ws_bytes > kScratchBytes) return MAMBA2_SCAN_ESCRATCH;

@@ -96,6 +96,9 @@ int mamba2_scan_fwd(int B, int K, int SH2, int STATE_D,
  *   workspace             workspace_bytes >= mamba2_scan_bwd_workspace_bytes
  * Equivalent to mamba2_scan_bwd_partials followed by mamba2_scan_bwd_reduce
  * on the same stream.  The weight gradients are bitwise reproducible.
+ * With STATE_D > 16 supports K * SH2 <= 2^26 (a 16-sample block's rows are
+ * addressed with 32-bit offsets; MAMBA2_SCAN_EUNSUPPORTED beyond, before
+ * any other check); STATE_D = 16 has no such limit.
  *
  * Why `saved` is required: the two pages differ on where the backward gets
  * the projections.  The plan's Task 2 step 4 reuses the forward's A/B

@@ -133,6 +133,21 @@ def test_bwd_argument_checks(L):
     assert L.mamba2_scan_bwd_reduce(*dims, ctypes.c_void_p(0x20004), ws, g, g, g, None) == m2.EALIGN
 
 
+def test_bwd_row_span_limit(L):
+    """With several state groups the backward addresses a block's rows with
+    32-bit offsets: K * SH2 above 2^26 is refused before any other check, and
+    only there (one state group has no such limit; a NULL pointer shows which
+    check ran)."""
+    big, edge = (16, 2 ** 18, 512, 32), (16, 2 ** 17, 512, 32)  # K * SH2 = 2^27, 2^26
+    for dims, code in ((big, m2.EUNSUPPORTED), (edge, m2.ENULL), ((16, 2 ** 18, 512, 16), m2.ENULL)):
+        assert L.mamba2_scan_bwd(*dims, None, None, None, 0, None, None, None, None, None, None, None, None, 0,
+                                 None) == code, dims
+        assert L.mamba2_scan_bwd_noalloc(*dims, None, None, None, 0, None, None, None, None, None, None, None,
+                                         None) == code, dims
+        assert L.mamba2_scan_bwd_bf16(*dims, None, None, None, 0, None, None, None, None, None, None, None, None,
+                                      0, None) == code, dims
+
+
 def test_bwd_input_argument_checks(L):
     dims = (100, 5, 192, 32)
     sv = m2.saved_bytes(*dims)
