@@ -1162,21 +1162,23 @@ __device__ __forceinline__ void bwd_compute(const BwdUnit& U, bool live, const C
 // product together, about one fp32 rounding); bf16 history values are
 // exact, so three products.  The result layout is that of the fp32 MFMAs.
 // Units per sample block: ceil(K/2) step pairs and the readout (its second
-// half carries d = 0).  A pair past the last step (odd K) re-reads step t0
-// with d masked to zero.  The history tiles are ordinary loads: the state
+// half carries d = 0).  The second step of the last pair of an odd K
+// re-reads step t0 with d masked to zero.  The history tiles are ordinary
+// loads: the state
 // groups' work-groups of a column block read them on one XCD and share them
 // through L2.  32768 samples, K = 8, SH2 = 512, STATE_D = 64: 400-403 ->
-// 333-337 us.  What remains is mostly VALU (the splits, the d values) and
-// memory: with the MFMAs taken out the kernel still took 289 us where it
-// took 351-361 us on the same machine.
+// 333-337 us (327-334 us with the buffer loads below).  What remains is
+// mostly VALU (the splits, the d values) and memory: with the MFMAs taken
+// out the kernel still took 289 us where it took 351-361 us on the same
+// machine.
 struct BwdPair {
   v4f h[2][4];   // A operands: step s, row i (sample 4kg+i), 4 features
   v2u hr[2][4];  // bf16 inputs: the same, as loaded
   v4f al[2];     // alpha'_t of each step (readout: x_K)
   v4f be[2];     // beta'_t of each step
   v4f sr;        // S_r of the pair's round (both steps share it: rounds are 8 steps)
-  float dc[4];   // d_context of samples 4kg+i, state n (unmasked)
-  int blk, tp, nvalid;  // block, pair (tp == ceil(K/2): readout), samples below B
+  float dc[4];   // d_context of samples 4kg+i, state n (0 for samples past B)
+  int blk, tp, nvalid;  // block, pair (tp == ceil(K/2): readout), samples from the block's first to B
 };
 
 // Buffer loads with per-lane byte offsets fixed for the work-group: a unit
