@@ -246,6 +246,26 @@ def test_noalloc_argument_checks(L):
 
 
 
+def test_backward_workspace_follows_the_unit_plan():
+    """The backward's split-K workspace is D/16 state groups x p0 slices x
+    SH2 x 48 floats, with p0 = min(ceil(256 / V), ceil(units / waves)) and
+    V = (SH2/64) * (D/16) work-group variants.  A sample block contributes
+    K step units and its readout with one state group (12 waves), and
+    ceil(K/2) step pairs and its readout with several (8 waves).  Checked
+    against the library's own plan over a sweep of shapes (host only)."""
+    for D in (16, 32, 64):
+        NG = D // 16
+        for SH2 in (64, 192, 256, 512):
+            V = (SH2 // 64) * NG
+            for K in (1, 2, 3, 8, 9, 64, 2048):
+                for B in (1, 16, 17, 100, 1000, 8192, 32768):
+                    NB = -(-B // 16)
+                    units = NB * ((K + 1) // 2 + 1 if NG > 1 else K + 1)
+                    waves = 8 if NG > 1 else 12
+                    p0 = min(-(-256 // V), -(-units // waves))
+                    assert m2.workspace_bytes(B, K, SH2, D) == NG * p0 * SH2 * 48 * 4, (B, K, SH2, D)
+
+
 def test_noalloc_scratch_covers_every_shape():
     """The allocation-free backward's 4 MiB buffer holds the split-K slices of
     every supported shape: a sweep over sample counts, history lengths, trunk
