@@ -2555,7 +2555,7 @@ size_t mamba2_scan_saved_bytes(int B, int K, int SH2, int STATE_D) {
 
 size_t mamba2_scan_bwd_workspace_bytes(int B, int K, int SH2, int STATE_D) {
   Plan pl;
-  return make_plan(B, K, SH2, STATE_D, &pl) == MAMBA2_SCAN_OK ? pl.ws_bytes : 0;
+  return make_plan(B, K, SH2, STATE_D, &pl) == MAMBA2_SCAN_OK && bwd_rows_fit(pl) ? pl.ws_bytes : 0;
 }
 
 int mamba2_scan_fwd(int B, int K, int SH2, int STATE_D, const float* h_history, const float* h_s2,

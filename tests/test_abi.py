@@ -139,6 +139,8 @@ def test_bwd_row_span_limit(L):
     only there (one state group has no such limit; a NULL pointer shows which
     check ran)."""
     big, edge = (16, 2 ** 18, 512, 32), (16, 2 ** 17, 512, 32)  # K * SH2 = 2^27, 2^26
+    assert m2.workspace_bytes(*big) == 0 and m2.workspace_bytes(*edge) > 0
+    assert m2.workspace_bytes(16, 2 ** 18, 512, 16) > 0
     for dims, code in ((big, m2.EUNSUPPORTED), (edge, m2.ENULL), ((16, 2 ** 18, 512, 16), m2.ENULL)):
         assert L.mamba2_scan_bwd(*dims, None, None, None, 0, None, None, None, None, None, None, None, None, 0,
                                  None) == code, dims
