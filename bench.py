@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ms per fwd+bwd scan step at B=8192,K=8,SH2=256,D=16; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published (bf16 trunk inputs run on these)
 SRC = os.path.join(ROOT, "bwd_mamba2_scan_amd", "csrc", "mamba2_scan.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pages_shape.json")
 MAX_STEPS = 2000  # steps of the one captured graph that is timed
@@ -556,13 +557,16 @@ def main():
     flops, per_kernel_flops = algorithmic_flops(B, K, SH2, D)
     dom = max(names, key=lambda n: kern_us[n])
     hbm_us = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
-    mfma_us = flops / (MFMA_FP32_PEAK_TFLOPS * 1e12) * 1e6
+    # the matrix-core peak of the contraction's own type: fp32 trunk inputs
+    # give an fp32 contraction, bf16 trunk inputs run on bf16 MFMAs
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if args.trunk == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    mfma_us = flops / (mfma_peak * 1e12) * 1e6
     roofline_us = max(hbm_us, mfma_us)
-    # the dominant kernel's own bound: bytes at HBM peak vs flops at fp32 MFMA peak
-    k_mfma = per_kernel_flops[dom] / (MFMA_FP32_PEAK_TFLOPS * 1e12) > per_kernel_bytes[dom] / (HBM_PEAK_GBS * 1e9)
+    # the dominant kernel's own bound: bytes at HBM peak vs flops at the MFMA peak
+    k_mfma = per_kernel_flops[dom] / (mfma_peak * 1e12) > per_kernel_bytes[dom] / (HBM_PEAK_GBS * 1e9)
     if k_mfma:
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(per_kernel_flops[dom] / (kern_us[dom] * 1e-6) / 1e12, 2),
-                "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s"}
+                "peak": mfma_peak, "unit": "TFLOP/s"}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(per_kernel_bytes[dom] / (kern_us[dom] * 1e-6) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
@@ -580,7 +584,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if args.trunk == "bf16" else "f32",
         "data": "synthetic",
         "config": {
             "workload": args.workload, "B": B, "K": K, "SH2": SH2, "STATE_D": D, "trunk": args.trunk,
